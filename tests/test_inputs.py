@@ -1,0 +1,49 @@
+"""The seeded input generators: determinism and the encoders against torch's
+own float32 -> fp16 / bf16 / float8_e4m3fn casts (round to nearest even)."""
+
+import numpy as np
+import torch
+
+from attention_forward_02_amd import inputs
+
+
+def test_encoders_match_torch_casts():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(200000).astype(np.float32) * s for s in (1e-3, 1.0, 30.0, 400.0)])
+    # ties and edge values
+    x = np.concatenate([x, np.float32([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -11, 0.0, -0.0])])
+    f16 = inputs.encode_f16(x)
+    assert np.array_equal(f16, torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16))
+    bf = inputs.encode_bf16(x)
+    assert np.array_equal(bf, torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    inr = np.abs(x) <= 448.0
+    e4 = inputs.encode_e4m3(x[inr])
+    ref = torch.from_numpy(x[inr]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(e4, ref)
+
+
+def test_e4m3_saturates_and_rounds_ties_to_even():
+    codes = inputs.encode_e4m3(np.array([1e9, -1e9, 460.0, 448.0, 1.0625, 1.1875, 2.0 ** -10, 1.5 * 2.0 ** -10]))
+    assert codes.tolist() == [0x7E, 0xFE, 0x7E, 0x7E, 0x38, 0x3A, 0x00, 0x01]
+
+
+def test_workloads_are_seeded_and_shaped():
+    a = inputs.make(1, 2, 33, 40, 64, "bf16", seed=7, causal=True)
+    b = inputs.make(1, 2, 33, 40, 64, "bf16", seed=7, causal=True)
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.k, b.k) and np.array_equal(a.v, b.v)
+    assert a.q.shape == (1, 2, 33, 64) and a.k.shape == (1, 2, 40, 64) and a.v.shape == (1, 2, 40, 64)
+    assert a.q.dtype == np.uint16 and a.scale == np.float32(1.0 / 8.0)
+    c = inputs.make(1, 1, 64, 64, 128, "e4m3", seed=3, outliers=True, keep_f32=True)
+    assert c.q.dtype == np.uint8
+    for x32, ds in zip((c.q32, c.k32, c.v32), c.descale):
+        assert ds == np.float32(np.abs(x32).max() / 448.0)
+    tiny = inputs.make_workload("tiny_d64_f16")
+    assert tiny.q.shape == (1, 1, 128, 64) and not tiny.causal
+    assert set(inputs.WORKLOADS) == {"tiny_d64_f16", "causal_d64_bf16", "hd128_seq8k_f16",
+                                     "causal_d256_bf16", "hd128_seq8k_e4m3"}
+
+
+def test_outliers_are_present():
+    c = inputs.make(1, 4, 1024, 1024, 128, "e4m3", seed=11, outliers=True, keep_f32=True)
+    frac = np.mean(np.abs(c.v32) > 8.0)
+    assert 3e-4 < frac < 2e-3

@@ -1,2 +1,29 @@
-"""MI355X (gfx950) fused attention forward: a C-ABI HIP library and its thin
-Python binding."""
+"""MI355X (gfx950) fused attention forward: a C-ABI HIP library
+(libattn.so, declared in include/attn.h) and its thin Python binding.
+
+    from attention_forward_02_amd import attention
+    o, lse = attention(q, k, v, causal=True)     # torch device tensors
+
+The library is loaded on first use; nothing here computes on the CPU.
+"""
+
+from .binding import (  # noqa: F401
+    ATTN_BF16,
+    ATTN_ERR_ALIAS,
+    ATTN_ERR_ALIGN,
+    ATTN_ERR_DTYPE,
+    ATTN_ERR_HEADDIM,
+    ATTN_ERR_LAUNCH,
+    ATTN_ERR_NULL,
+    ATTN_ERR_SCALE,
+    ATTN_ERR_SHAPE,
+    ATTN_F16,
+    ATTN_FP8_E4M3,
+    ATTN_OK,
+    AttnError,
+    attention,
+    attn_fwd,
+    attn_fwd_fp8,
+    attn_status_str,
+    load_library,
+)

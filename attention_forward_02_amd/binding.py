@@ -1,0 +1,140 @@
+"""Thin ctypes binding of libattn.so (argument marshalling only).
+
+The C functions keep their names: ``attn_fwd``, ``attn_fwd_fp8`` and
+``attn_status_str`` take the same arguments as in include/attn.h, with any
+pointer given either as an integer device address or as a torch tensor
+(its ``data_ptr()``), and the stream as a torch stream, an integer handle or
+None (the current torch stream).  ``attention`` is a convenience wrapper that
+allocates the outputs with torch and raises ``AttnError`` on a non-zero
+status.  Every step of the computation runs in the HIP library; if the
+library is missing, calls raise instead of falling back to anything else.
+"""
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn.so")
+
+ATTN_F16 = 0
+ATTN_BF16 = 1
+ATTN_FP8_E4M3 = 2
+
+ATTN_OK = 0
+ATTN_ERR_NULL = -1
+ATTN_ERR_SHAPE = -2
+ATTN_ERR_HEADDIM = -3
+ATTN_ERR_DTYPE = -4
+ATTN_ERR_ALIGN = -5
+ATTN_ERR_SCALE = -6
+ATTN_ERR_LAUNCH = -7
+ATTN_ERR_ALIAS = -8
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status):
+        super().__init__(f"attn status {status}: {attn_status_str(status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libattn.so once and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m attention_forward_02_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.attn_fwd.restype = ci
+    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, cf, cf, cf, vp]
+    lib.attn_fwd_fp8.restype = ci
+    lib.attn_status_str.argtypes = [ci]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    return int(s)
+
+
+def attn_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, stream=None):
+    """The C ``attn_fwd``; returns its status code."""
+    lib = load_library()
+    return lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
+                        int(d), int(bool(causal)), float(scale), int(dtype), _stream(stream))
+
+
+def attn_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, q_descale, k_descale, v_descale,
+                 stream=None):
+    """The C ``attn_fwd_fp8``; returns its status code."""
+    lib = load_library()
+    return lib.attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
+                            int(d), int(bool(causal)), float(scale), float(q_descale), float(k_descale),
+                            float(v_descale), _stream(stream))
+
+
+def attn_status_str(status):
+    return load_library().attn_status_str(int(status)).decode()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", None)):
+        return ATTN_FP8_E4M3
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+def attention(q, k, v, causal=False, scale=None, descale=None, stream=None):
+    """O, LSE for contiguous device tensors q [B,H,Nq,d], k, v [B,H,Nk,d].
+
+    fp16 -> fp16 O, bf16 -> bf16 O, e4m3 (float8_e4m3fn or uint8 codes) ->
+    fp16 O with ``descale = (q_descale, k_descale, v_descale)``.  LSE is
+    float32 [B,H,Nq].  Runs on ``stream`` (default: current torch stream)
+    without synchronising.
+    """
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    code = _dtype_code(q)
+    if _dtype_code(k) != code or _dtype_code(v) != code:
+        raise TypeError("q, k, v must share one dtype")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out_dtype = torch.bfloat16 if code == ATTN_BF16 else torch.float16
+    o = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if code == ATTN_FP8_E4M3:
+        qd, kd, vd = descale if descale is not None else (1.0, 1.0, 1.0)
+        st = attn_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, qd, kd, vd, stream)
+    else:
+        st = attn_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, code, stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return o, lse

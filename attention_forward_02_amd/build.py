@@ -1,0 +1,67 @@
+"""Build libattn.so (the C-ABI HIP library) in-tree with hipcc for gfx950.
+
+Usage: python -m attention_forward_02_amd.build [-v]
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libattn.so")
+SOURCES = ["attn_api.cpp", "attn_fwd.hip"]
+ARCH = "gfx950"
+
+
+def hipcc():
+    for cand in (os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc"), shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; set ROCM_PATH")
+
+
+def command(out=LIB):
+    return [
+        hipcc(),
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-shared",
+        # Packed FP32 VALU forms stay off: hipcc would otherwise emit them
+        # from ordinary float2 arithmetic.  The host pass ignores the flag.
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-command-line-argument",
+        # MFMA accumulators in ordinary VGPRs: the softmax rescales them
+        # every tile, and AGPR-resident accumulators would need copies.
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
+        "-I", INCLUDE,
+        "-I", CSRC,
+        *[os.path.join(CSRC, s) for s in SOURCES],
+        "-o", out,
+    ]
+
+
+def build(verbose=False):
+    """Compile every source into libattn.so next to this file (always
+    recompiles) and return its path."""
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    if verbose and res.stderr.strip():
+        sys.stderr.write(res.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,97 @@
+// C ABI of the fused attention forward library: argument validation and
+// dispatch.  Declarations and the full contract are in include/attn.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Half-open byte ranges [a, a+na) and [b, b+nb) overlap.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+bool positive_finite(float x) { return isfinite(x) && x > 0.f; }
+
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+             int Nq, int Nk, int d, int dtype) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_HEADDIM;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_DTYPE;
+  const long long nq = (long long)B * H * Nq * d, nk = (long long)B * H * Nk * d;
+  if (nq >= (1LL << 31) || nk >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return ATTN_ERR_ALIGN;
+  const size_t in_elt = dtype == ATTN_FP8_E4M3 ? 1 : 2;
+  const size_t qb = (size_t)nq * in_elt, kb = (size_t)nk * in_elt;
+  const size_t ob = (size_t)nq * 2, lb = (size_t)B * H * Nq * sizeof(float);
+  if (overlap(o, ob, q, qb) || overlap(o, ob, k, kb) || overlap(o, ob, v, kb) || overlap(o, ob, lse, lb) ||
+      overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb))
+    return ATTN_ERR_ALIAS;
+  return ATTN_OK;
+}
+
+int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
+        int causal, float scale, int dtype, float q_ds, float k_ds, float v_ds, ihipStream_t* stream) {
+  int st = validate(q, k, v, o, lse, B, H, Nq, Nk, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!positive_finite(scale) || !positive_finite(q_ds) || !positive_finite(k_ds) || !positive_finite(v_ds))
+    return ATTN_ERR_SCALE;
+  const float s = scale * q_ds * k_ds;
+  if (!positive_finite(s)) return ATTN_ERR_SCALE;
+  attn::Problem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.d = d;
+  p.causal = causal != 0;
+  p.dtype = dtype;
+  p.scale = s;
+  p.v_descale = v_ds;
+  return attn::launch_forward(p, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+             int d, int causal, float scale, int dtype, ihipStream_t* stream) {
+  return run(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, 1.f, 1.f, 1.f, stream);
+}
+
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                 int Nk, int d, int causal, float scale, float q_descale, float k_descale, float v_descale,
+                 ihipStream_t* stream) {
+  return run(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, ATTN_FP8_E4M3, q_descale, k_descale, v_descale,
+             stream);
+}
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "B, H, Nq and Nk must be >= 1 and each tensor < 2^31 elements";
+    case ATTN_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
+    case ATTN_ERR_DTYPE: return "unknown dtype";
+    case ATTN_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case ATTN_ERR_SCALE: return "scale and descales must be finite and > 0";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_ALIAS: return "o or lse overlaps an input or the other output";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

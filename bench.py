@@ -1,0 +1,164 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one attn_fwd call over the whole workload (default: B=2, H=16,
+Nq=Nk=8192, d=128, non-causal fp16), inputs resident in HBM before timing.
+Prints ONE JSON line with TFLOP/s (4*B*H*Nq*Nk*d, halved for causal), the
+MFMA roofline of the kernel, and the float64 CPU oracle timed on a bounded
+sample of the same workload on this machine's host cores.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPs/s and % of MFMA peak, hdim128 seq8192 fp16, 1 GPU"
+
+# MI355X dense MFMA peaks (TFLOP/s): 256 CUs x 2.4 GHz x FLOP/clk/CU.
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2}
+
+
+def _cpu_baseline(inp, budget_s):
+    """Time the oracle (as it stands) on whole 512-row query chunks of the
+    workload's heads, in order, until about `budget_s` seconds of CPU work."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity set
+        threads = len(os.sched_getaffinity(0))
+    dec = {"f16": oracle.decode_f16, "bf16": oracle.decode_bf16, "e4m3": oracle.decode_e4m3}[inp.dtype]
+    qd, kd, vd = (float(x) for x in inp.descale)
+    chunk = 512
+    flops = 0.0
+    spent = 0.0
+    done_rows = 0
+    heads = 0
+    for b in range(inp.B):
+        for h in range(inp.H):
+            q = dec(inp.q[b, h])[None, None] * qd
+            k = dec(inp.k[b, h])[None, None] * kd
+            v = dec(inp.v[b, h])[None, None] * vd
+            heads += 1
+            for r0 in range(0, inp.Nq, chunk):
+                rows = np.arange(r0, min(inp.Nq, r0 + chunk))
+                t0 = time.perf_counter()
+                oracle.attention(q, k, v, inp.causal, float(inp.scale), rows=rows)
+                spent += time.perf_counter() - t0
+                if inp.causal:
+                    nk_eff = np.minimum(rows + (inp.Nk - inp.Nq) + 1, inp.Nk).clip(min=0).sum()
+                    flops += 4.0 * nk_eff * inp.d
+                else:
+                    flops += 4.0 * len(rows) * inp.Nk * inp.d
+                done_rows += len(rows)
+                if spent >= budget_s:
+                    break
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOPs/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{done_rows} query rows ({chunk}-row chunks) of {heads} of {inp.B * inp.H} heads, "
+                   f"{spent:.1f} s, float64 numpy oracle, same FLOP count convention"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="hd128_seq8k_f16")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this attention forward has no multi-GPU path "
+              "(heads shard across GPUs with no communication); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from attention_forward_02_amd import inputs
+    from attention_forward_02_amd.binding import attn_fwd, attn_fwd_fp8, ATTN_F16, ATTN_BF16, ATTN_OK, AttnError
+
+    w = inputs.WORKLOADS[args.workload]
+    inp = inputs.make_workload(args.workload)
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        if inp.dtype == "e4m3":
+            return torch.from_numpy(bits).view(torch.float8_e4m3fn).to(dev)
+        return torch.from_numpy(bits.view(np.int16)).view(torch.float16 if inp.dtype == "f16" else torch.bfloat16).to(dev)
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    out_dt = torch.bfloat16 if inp.dtype == "bf16" else torch.float16
+    o = torch.empty((inp.B, inp.H, inp.Nq, inp.d), dtype=out_dt, device=dev)
+    lse = torch.empty((inp.B, inp.H, inp.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    code = {"f16": ATTN_F16, "bf16": ATTN_BF16}.get(inp.dtype)
+
+    def step():
+        if inp.dtype == "e4m3":
+            st = attn_fwd_fp8(q, k, v, o, lse, inp.B, inp.H, inp.Nq, inp.Nk, inp.d, inp.causal, float(inp.scale),
+                              *(float(x) for x in inp.descale), stream)
+        else:
+            st = attn_fwd(q, k, v, o, lse, inp.B, inp.H, inp.Nq, inp.Nk, inp.d, inp.causal, float(inp.scale),
+                          code, stream)
+        if st != ATTN_OK:
+            raise AttnError(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    fl = inputs.flops(inp.B, inp.H, inp.Nq, inp.Nk, inp.d, inp.causal)
+    tflops = fl / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[inp.dtype]
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOPs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic: seeded i.i.d. N(0,1) inputs",
+        "config": {"workload": args.workload, "B": inp.B, "H": inp.H, "Nq": inp.Nq, "Nk": inp.Nk, "d": inp.d,
+                   "causal": inp.causal, "in_dtype": inp.dtype, "flops_per_step": fl},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "kernel": "attn_fwd_kernel", "flops_per_launch": fl},
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = _cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,111 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention forward library.
+ *
+ * The operation is the attention forward pass with per-row log-sum-exp,
+ * computed block by block with a running row max and row sum so that the
+ * Nq x Nk score matrix never reaches device memory:
+ *
+ *   S   = scale * Q K^T                       (per batch b and head h)
+ *   P   = softmax(S) over keys, row by row    (causal: only allowed keys)
+ *   O   = P V
+ *   LSE = m + ln(sum_j exp(S_ij - m)),  m = max_j S_ij   (natural log)
+ *
+ * Source: "Warp specialization" concept card (wikillm), "Implementation
+ * sketch": a block of queries with keys and values streamed from global
+ * memory yields the output block and one log-sum-exp per row, returned as
+ * (output / row_sum, row_max + log(row_sum)).  The FP8 E4M3 variant with
+ * per-tensor scaling is section 5 of "Inside FlashAttention-3 &
+ * Warp-Specialized CUDA Kernels" (tekromancy.com).  The pages describe one
+ * key/value tile stream per (batch, head) of a (B, H, N, D) tensor.
+ *
+ * Layout (all tensors dense, row-major, innermost dimension contiguous):
+ *   q   [B][H][Nq][d]     element type per `dtype`
+ *   k   [B][H][Nk][d]     same type as q
+ *   v   [B][H][Nk][d]     same type as q
+ *   o   [B][H][Nq][d]     f16 for ATTN_F16 and ATTN_FP8_E4M3, bf16 for ATTN_BF16
+ *   lse [B][H][Nq]        float32
+ *
+ * Causal masking keeps key j for query i iff j <= i + (Nk - Nq)
+ * (bottom-right alignment; identical to j <= i when Nq == Nk).  A query row
+ * that sees no key (causal with Nq > Nk) gets O = 0 and LSE = -inf.
+ *
+ * Ownership: every pointer is a DEVICE pointer allocated and owned by the
+ * caller.  The library allocates nothing, keeps no mutable global state, and
+ * is safe to call from several host threads.  o and lse must not overlap the
+ * inputs or each other.
+ *
+ * Stream: the call validates its arguments on the host, enqueues the work on
+ * `stream` (NULL = the default stream) and returns without synchronising.
+ *
+ * Errors: validation happens before anything touches the device; a rejected
+ * call returns a negative ATTN_ERR_* code and enqueues nothing.  A failed
+ * launch returns ATTN_ERR_LAUNCH.  Faults during execution surface on the
+ * stream when the caller synchronises.  The library never aborts or prints.
+ */
+#ifndef ATTN_MI355X_ATTN_H
+#define ATTN_MI355X_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t. */
+struct ihipStream_t;
+
+typedef enum {
+  ATTN_F16 = 0,       /* IEEE binary16 in, binary16 out */
+  ATTN_BF16 = 1,      /* bfloat16 in, bfloat16 out */
+  ATTN_FP8_E4M3 = 2   /* OCP FP8 E4M3 ("fn") in, binary16 out */
+} attn_dtype;
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,     /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,    /* B, H, Nq or Nk < 1, or a tensor has >= 2^31 elements */
+  ATTN_ERR_HEADDIM = -3,  /* d not in {64, 128, 256} */
+  ATTN_ERR_DTYPE = -4,    /* unknown dtype code */
+  ATTN_ERR_ALIGN = -5,    /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
+  ATTN_ERR_SCALE = -6,    /* scale or a descale is not finite and > 0 */
+  ATTN_ERR_LAUNCH = -7,   /* the kernel launch failed */
+  ATTN_ERR_ALIAS = -8     /* o or lse overlaps an input or the other output */
+};
+
+/*
+ * attn_fwd: one fused attention forward over all B*H (batch, head) pairs.
+ *
+ * q, k, v  device inputs, layout above, element type `dtype`
+ * o, lse   device outputs, layout above (every element is written)
+ * B, H     batch size and heads (>= 1)
+ * Nq, Nk   query and key counts (>= 1; need not be multiples of any tile)
+ * d        head dimension: 64, 128 or 256
+ * causal   0 = full attention, nonzero = bottom-right causal mask
+ * scale    multiplies Q K^T before the softmax (finite, > 0), e.g. 1/sqrt(d)
+ * dtype    an attn_dtype; ATTN_FP8_E4M3 here means unit descales
+ * stream   HIP stream to enqueue on (NULL = default stream)
+ *
+ * Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Nq, int Nk, int d, int causal, float scale,
+             int dtype, struct ihipStream_t* stream);
+
+/*
+ * attn_fwd_fp8: the FP8 E4M3 forward with per-tensor scaling ("Inside
+ * FlashAttention-3", section 5).  The real value of each input element is
+ * its E4M3 code times that tensor's descale.  Scores accumulate in fp32;
+ * the probabilities are rounded to E4M3 for the P V product; O is binary16.
+ * Arguments as attn_fwd, plus q_descale, k_descale, v_descale (finite, > 0).
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                 float q_descale, float k_descale, float v_descale,
+                 struct ihipStream_t* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_ATTN_H */

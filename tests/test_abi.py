@@ -1,0 +1,103 @@
+"""The C-ABI library on the CPU: it loads, exports every function that
+include/attn.h declares, and rejects every invalid argument with the
+documented code before touching the device (no call here reaches a launch;
+the fake device addresses below are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_forward_02_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _lib():
+    if not os.path.exists(b.LIB_PATH):
+        pytest.fail("libattn.so is not built (python -m attention_forward_02_amd.build)")
+    return b.load_library()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", src, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    assert set(_declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_status_str"}
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_codes_match_header():
+    src = open(HEADER).read()
+    codes = dict((k, int(v)) for k, v in re.findall(r"(ATTN_(?:OK|ERR_\w+))\s*=\s*(-?\d+)", src))
+    for name, val in codes.items():
+        assert getattr(b, name) == val, name
+    dts = dict((k, int(v)) for k, v in re.findall(r"(ATTN_(?:F16|BF16|FP8_E4M3))\s*=\s*(\d+)", src))
+    assert dts == {"ATTN_F16": b.ATTN_F16, "ATTN_BF16": b.ATTN_BF16, "ATTN_FP8_E4M3": b.ATTN_FP8_E4M3}
+    lib = _lib()
+    for val in codes.values():
+        s = lib.attn_status_str(val)
+        assert s and len(s) > 1
+    assert lib.attn_status_str(12345) == b"unknown status"
+
+
+# Fake, aligned, non-overlapping device addresses: validation must reject the
+# call before anything is dereferenced or launched.
+Q, K, V, O, L = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+GOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Nq=128, Nk=128, d=64, causal=0, scale=0.125, dtype=0)
+
+
+def _call(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    lib = _lib()
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                        a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), b.ATTN_ERR_NULL), (dict(k=None), b.ATTN_ERR_NULL), (dict(v=None), b.ATTN_ERR_NULL),
+    (dict(o=None), b.ATTN_ERR_NULL), (dict(lse=None), b.ATTN_ERR_NULL),
+    (dict(B=0), b.ATTN_ERR_SHAPE), (dict(H=-1), b.ATTN_ERR_SHAPE), (dict(Nq=0), b.ATTN_ERR_SHAPE),
+    (dict(Nk=0), b.ATTN_ERR_SHAPE), (dict(B=1 << 12, H=1 << 10, Nq=1 << 10), b.ATTN_ERR_SHAPE),
+    (dict(d=96), b.ATTN_ERR_HEADDIM), (dict(d=32), b.ATTN_ERR_HEADDIM), (dict(d=512), b.ATTN_ERR_HEADDIM),
+    (dict(dtype=3), b.ATTN_ERR_DTYPE), (dict(dtype=-1), b.ATTN_ERR_DTYPE),
+    (dict(q=Q + 8), b.ATTN_ERR_ALIGN), (dict(o=O + 2), b.ATTN_ERR_ALIGN), (dict(lse=L + 2), b.ATTN_ERR_ALIGN),
+    (dict(scale=float("nan")), b.ATTN_ERR_SCALE), (dict(scale=float("inf")), b.ATTN_ERR_SCALE),
+    (dict(scale=0.0), b.ATTN_ERR_SCALE), (dict(scale=-0.5), b.ATTN_ERR_SCALE),
+    (dict(o=Q), b.ATTN_ERR_ALIAS), (dict(o=Q + 16), b.ATTN_ERR_ALIAS), (dict(lse=V + 4096), b.ATTN_ERR_ALIAS),
+    (dict(lse=O + 1024), b.ATTN_ERR_ALIAS),
+])
+def test_validation_rejects_before_launch(kw, code):
+    assert _call(**kw) == code
+
+
+def test_fp8_descales_validated():
+    lib = _lib()
+    a = GOOD
+    for qd, kd, vd in [(0.0, 1.0, 1.0), (1.0, float("nan"), 1.0), (1.0, 1.0, -2.0), (1e30, 1e30, 1.0)]:
+        st = lib.attn_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 2, 128, 128, 64, 0, 0.125,
+                              qd, kd, vd, None)
+        assert st == b.ATTN_ERR_SCALE
+    st = lib.attn_fwd_fp8(None, a["k"], a["v"], a["o"], a["lse"], 1, 2, 128, 128, 64, 0, 0.125, 1.0, 1.0, 1.0, None)
+    assert st == b.ATTN_ERR_NULL
+
+
+def test_binding_raises_without_library(tmp_path):
+    saved = b._lib
+    b._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            b.load_library(str(tmp_path / "missing.so"))
+    finally:
+        b._lib = saved

@@ -1,0 +1,154 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs.  Tolerances are stated in tests/gpu_helpers.py.
+
+* every named workload: small ones element by element on all rows; the
+  full-size ones (B=2,H=16,N=8192,d=128 and B=1,H=16,N=16384,d=256 causal)
+  on sampled rows of sampled heads, in the launch configuration the
+  benchmark times;
+* edge shapes: N in {1, 17, 127, 129, 1000}, Nq != Nk both ways (including
+  causal rows with no visible key), every head dim, both 16-bit dtypes;
+* invariants on the device: V = 1, Q = 0, bitwise determinism, a
+  non-default stream, and canaries past the ends of o and lse.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_forward_02_amd import attn_fwd, inputs, ATTN_F16, ATTN_BF16, ATTN_OK
+from gpu_helpers import compare, dequant, run_gpu, say, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_check(inp, label):
+    say(f"[gpu] {label}: B={inp.B} H={inp.H} Nq={inp.Nq} Nk={inp.Nk} d={inp.d} "
+        f"causal={inp.causal} dtype={inp.dtype}")
+    o_codes, lse = run_gpu(inp)
+    q, k, v = dequant(inp)
+    o_ref, lse_ref = oracle.attention(q, k, v, inp.causal, float(inp.scale))
+    stats = compare(o_codes, lse, o_ref, lse_ref, inp.dtype, label)
+    say(f"[gpu] {label}: {stats}")
+    return stats
+
+
+def _sampled_check(inp, label, heads, n_rows, seed):
+    say(f"[gpu] {label}: B={inp.B} H={inp.H} Nq={inp.Nq} Nk={inp.Nk} d={inp.d} "
+        f"causal={inp.causal} dtype={inp.dtype} (sampled)")
+    o_codes, lse = run_gpu(inp)
+    o2, lse2 = run_gpu(inp)
+    assert np.array_equal(o_codes, o2) and np.array_equal(lse, lse2), "repeat runs differ"
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, inp.Nq // 2, inp.Nq - 2, inp.Nq - 1],
+                                     rng.choice(inp.Nq, n_rows, replace=False)]))
+    q, k, v = dequant(inp, heads)
+    o_ref, lse_ref = oracle.attention(q, k, v, inp.causal, float(inp.scale), rows=rows)
+    o_sel = np.stack([o_codes[b, h][rows] for b, h in heads])[None]
+    l_sel = np.stack([lse[b, h][rows] for b, h in heads])[None]
+    stats = compare(o_sel, l_sel, o_ref, lse_ref, inp.dtype, label)
+    # every output of the whole tensor is finite and every LSE at least the row's own score bound
+    assert np.isfinite(lse).all()
+    say(f"[gpu] {label}: {stats} over {len(heads)} heads x {len(rows)} rows")
+    return stats
+
+
+def test_tiny_d64_f16():
+    _full_check(inputs.make_workload("tiny_d64_f16"), "tiny_d64_f16")
+
+
+def test_causal_d64_bf16():
+    _full_check(inputs.make_workload("causal_d64_bf16"), "causal_d64_bf16")
+
+
+def test_hd128_seq8k_f16_sampled():
+    inp = inputs.make_workload("hd128_seq8k_f16")
+    _sampled_check(inp, "hd128_seq8k_f16", heads=[(0, 0), (0, 9), (1, 4), (1, 15)], n_rows=48, seed=1)
+
+
+def test_causal_d256_bf16_sampled():
+    inp = inputs.make_workload("causal_d256_bf16")
+    _sampled_check(inp, "causal_d256_bf16", heads=[(0, 0), (0, 7), (0, 15)], n_rows=40, seed=2)
+
+
+EDGE_N = [(1, 1), (17, 17), (127, 127), (129, 129), (1000, 1000), (1, 1000), (17, 129), (129, 17),
+          (1000, 127), (300, 77)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", EDGE_N, ids=[f"{a}x{b}" for a, b in EDGE_N])
+def test_edge_shapes(nq, nk, causal, d, dtype):
+    seed = 7 + nq * 31 + nk * 17 + d + (1 if causal else 0)
+    inp = inputs.make(1, 2, nq, nk, d, dtype, seed=seed, causal=causal)
+    _full_check(inp, f"edge {nq}x{nk} d{d} {'causal' if causal else 'full'} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_invariants_on_device(dtype):
+    B, H, N, d = 2, 3, 333, 128
+    inp = inputs.make(B, H, N, N, d, dtype, seed=99)
+    dt = torch.float16 if dtype == "f16" else torch.bfloat16
+    q, k, v = upload(inp.q, dtype), upload(inp.k, dtype), upload(inp.v, dtype)
+    from attention_forward_02_amd import attention
+    for causal in (False, True):
+        say(f"[gpu] invariants {dtype} causal={causal}: V = 1")
+        o, _ = attention(q, k, torch.ones_like(v), causal=causal)
+        torch.cuda.synchronize()
+        assert torch.allclose(o.float(), torch.ones_like(o, dtype=torch.float32), atol=4e-3, rtol=0)
+        say(f"[gpu] invariants {dtype} causal={causal}: Q = 0")
+        o, lse = attention(torch.zeros_like(q), k, v, causal=causal)
+        torch.cuda.synchronize()
+        vv = dequant(inp)[2]
+        if causal:
+            mean = np.cumsum(vv, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+            n = np.arange(1, N + 1, dtype=np.float64)
+        else:
+            mean = np.broadcast_to(vv.mean(axis=2, keepdims=True), vv.shape)
+            n = np.full(N, float(N))
+        od = o.float().cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(od, mean, rtol=0, atol=4e-3 if dtype == "f16" else 1.6e-2)
+        np.testing.assert_allclose(lse.cpu().numpy(), np.broadcast_to(np.log(n), (B, H, N)), rtol=0, atol=1e-4)
+        if causal:
+            # row 0 sees key 0 only: O0 = V0 exactly (rounded to the output type)
+            assert torch.equal(o[:, :, 0], v[:, :, 0])
+
+
+def test_determinism_stream_and_canaries():
+    inp = inputs.make(2, 4, 777, 777, 128, "f16", seed=5, causal=True)
+    q, k, v = upload(inp.q, "f16"), upload(inp.k, "f16"), upload(inp.v, "f16")
+    B, H, N, d = 2, 4, 777, 128
+    n_o, n_l, pad = B * H * N * d, B * H * N, 4096
+    sentinel_o = torch.tensor([0x7BCD], dtype=torch.int16).view(torch.float16)  # 63904.0
+    results = []
+    for use_stream in (False, True):
+        say(f"[gpu] determinism/canary run, non-default stream={use_stream}")
+        o_buf = torch.full((n_o + pad,), float(sentinel_o), dtype=torch.float16, device="cuda")
+        l_buf = torch.full((n_l + pad,), 12345.0, dtype=torch.float32, device="cuda")
+        stream = torch.cuda.Stream() if use_stream else torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            st = attn_fwd(q, k, v, o_buf, l_buf, B, H, N, N, d, True, float(inp.scale), ATTN_F16, stream)
+        assert st == ATTN_OK
+        stream.synchronize()
+        assert torch.all(o_buf[n_o:] == sentinel_o.item()), "write past the end of o"
+        assert torch.all(l_buf[n_l:] == 12345.0), "write past the end of lse"
+        assert not torch.any(o_buf[:n_o] == sentinel_o.item()), "an output element was not written"
+        results.append((o_buf[:n_o].clone(), l_buf[:n_l].clone()))
+    assert torch.equal(results[0][0].view(torch.int16), results[1][0].view(torch.int16))
+    assert torch.equal(results[0][1], results[1][1])
+    q64, k64, v64 = dequant(inp)
+    o_ref, l_ref = oracle.attention(q64, k64, v64, True, float(inp.scale))
+    o_codes = results[0][0].view(torch.int16).cpu().numpy().view(np.uint16).reshape(B, H, N, d)
+    compare(o_codes, results[0][1].cpu().numpy().reshape(B, H, N), o_ref, l_ref, "f16", "canary run")
+
+
+def test_rejects_invalid_call_on_device():
+    inp = inputs.make(1, 1, 64, 64, 64, "bf16", seed=1)
+    q, k, v = upload(inp.q, "bf16"), upload(inp.k, "bf16"), upload(inp.v, "bf16")
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 1, 64), dtype=torch.float32, device="cuda")
+    from attention_forward_02_amd import ATTN_ERR_HEADDIM, ATTN_ERR_ALIAS
+    assert attn_fwd(q, k, v, o, lse, 1, 1, 64, 64, 80, False, 0.125, ATTN_BF16) == ATTN_ERR_HEADDIM
+    assert attn_fwd(q, k, v, q, lse, 1, 1, 64, 64, 64, False, 0.125, ATTN_BF16) == ATTN_ERR_ALIAS

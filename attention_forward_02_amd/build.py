@@ -39,6 +39,8 @@ def command(out=LIB):
         # MFMA accumulators in ordinary VGPRs: the softmax rescales them
         # every tile, and AGPR-resident accumulators would need copies.
         "-mllvm", "-amdgpu-mfma-vgpr-form",
+        # No NaN-quieting copies around fmaxf in the row-max reductions.
+        "-fno-honor-nans",
         "-I", INCLUDE,
         "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],

@@ -30,7 +30,7 @@
 #include "attn_internal.h"
 
 namespace attn {
-namespace {
+namespace kernels {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -42,6 +42,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -77,9 +78,8 @@ struct Elt<ATTN_F16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t pack(float x, float y) {
-    f16x2 h = {(_Float16)x, (_Float16)y};
-    return __builtin_bit_cast(uint32_t, h);
+  static __device__ __forceinline__ uint32_t pack(float x, float y) {  // v_cvt_pk_f16_f32 (RNE)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, f16x2));
   }
 };
 
@@ -89,18 +89,28 @@ struct Elt<ATTN_BF16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t pack(float x, float y) {
-    bf16x2 h = {(__bf16)x, (__bf16)y};
-    return __builtin_bit_cast(uint32_t, h);
+  static __device__ __forceinline__ uint32_t pack(float x, float y) {  // v_cvt_pk_bf16_f32 (RNE)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
   }
 };
 
-// XOR swizzle of the 16-byte chunk index within a row, by the row's low 3
-// bits.  Within any 8 consecutive rows the swizzle values are distinct, and
-// within any 4-aligned group of 4 rows their bits [2:1] are distinct, which
-// spreads both the K operand reads (8 rows, same chunk) and the V transpose
-// reads (4 rows x 2 adjacent chunks) over distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// XOR swizzle of the 16-byte chunk index within a row.  The gfx950 LDS
+// serves 256 bytes (64 banks x 4 B) per cycle, i.e. 16 lanes of a 128-bit
+// read or 32 lanes of a 64-bit read.  Two access patterns must be
+// conflict-free:
+//   * K operand reads (ds_read_b128): 16 consecutive rows, one logical chunk;
+//   * V transpose reads (ds_read_b64_tr_b16): 4 consecutive rows (a 4-aligned
+//     group) x 4 consecutive chunks (a 4-aligned group).
+// Rows of >= 256 bytes (d >= 128): f(r) = 4*(r&3) + ((r>>2)&3) is a bijection
+// on r mod 16, and inside a 4-row group its values differ in bits [3:2].
+// Rows of 128 bytes (d = 64) put two rows in one 256-byte bank window: f(r)
+// = 4*((r>>1)&1) + ((r>>2)&3) is distinct over the even and over the odd
+// rows of any 16, and rows r, r+2 of a 4-row group differ in bit 2.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return ((row & 2) << 1) | ((row >> 2) & 3);
+}
 
 __device__ __forceinline__ float swap_halves_max(float x) {
   // v_permlane32_swap with both operands x: result[0] holds lanes 0..31 of x
@@ -129,121 +139,215 @@ __device__ __forceinline__ void schedule(const Params& p, int bid, bool causal, 
   if (causal) qt = p.n_qtiles - 1 - qt;
 }
 
-// One wave's share of the direct-to-LDS loads of a [kBlockN x D] tile.
+// Direct-to-LDS tile loader for one wave (buffer_load_dwordx4 ... lds).
 // Every wave instruction fills 1 KB of LDS contiguously (lane i -> bytes
 // 16i..16i+15), so the swizzle is applied on the global side: LDS chunk
-// position pc of row r receives global chunk pc ^ swz(r).  Rows past Nk are
-// clamped to row Nk-1 (valid memory; such keys are masked to -inf, so their
-// values never reach the output).
+// position pc of row r receives global chunk pc ^ swz(r).  The buffer
+// resource spans exactly one head's [Nk x D] rows, so rows past Nk (a ragged
+// last tile) fail the hardware range check and arrive as zeros; their
+// scores are masked to -inf and their zero values meet P = 0.
 template <int D>
-__device__ __forceinline__ void load_tile(lds_t* dst, const uint16_t* src, int key0, int Nk, int wave,
-                                          int lane) {
-  constexpr int kRowBytes = D * 2;
-  constexpr int kChunks = D / 8;
-  constexpr int kRowsPerKB = 1024 / kRowBytes;
-  constexpr int kBlocks = kBlockN * kRowBytes / 1024;
+struct TileLoader {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;
+  static constexpr int kRowsPerKB = 1024 / kRowBytes;
+  static constexpr int kBlocks = kBlockN * kRowBytes / 1024;
+  static constexpr int kPerWave = kBlocks / kWaves;
   static_assert(kBlocks % kWaves == 0, "tile must split evenly over waves");
+  int voff[kPerWave];   // byte offset of this lane's chunk within a tile
+  int lds[kPerWave];    // LDS byte offset of the wave instruction's 1 KB block
+
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < kBlocks / kWaves; ++i) {
-    const int b = i * kWaves + wave;
-    const int row = b * kRowsPerKB + lane / kChunks;
-    const int chunk = (lane % kChunks) ^ swz(row);
-    const int key = min(key0 + row, Nk - 1);
-    const uint16_t* g = src + (size_t)key * D + chunk * 8;
-    __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)(dst + b * 1024),
-                                     16, 0, 0);
+    for (int i = 0; i < kPerWave; ++i) {
+      const int b = i * kWaves + wave;
+      const int row = b * kRowsPerKB + lane / kChunks;
+      voff[i] = row * kRowBytes + ((lane % kChunks) ^ swz<D>(row)) * 16;
+      lds[i] = b * 1024;
+    }
   }
+  __device__ __forceinline__ void load(lds_t* dst, __amdgpu_buffer_rsrc_t src, int key0) const {
+    const int tile = key0 * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(dst + lds[i]), 16,
+                                               voff[i] + tile, 0, 0, 0);
+  }
+};
+
+// Buffer resource over `bytes` bytes at `base` (raw, stride 0; gfx9 word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
 }
 
 // Per-wave state carried across key tiles.
 template <int D>
 struct WaveState {
+  static constexpr int kKOff = (D / 16 < 8) ? D / 16 : 8;
   i16x8 qf[D / 16];       // Q rows of this lane as MFMA B-operand fragments
   f32x16 oacc[D / 32];    // O^T accumulator, 32 output columns per block
-  float m2;               // running row max, in units of scale*log2(e)
+  float m2;               // reference row max for exp2, in units of scale*log2(e)
   float lrun;             // running row sum over this lane's half of the keys
-  int koff[4];            // per-lane LDS byte offsets of K operand reads
-  int voff[2];            // per-lane LDS byte offsets of V transpose reads
-};
+  int koff[kKOff];        // per-lane LDS byte offsets of K operand reads
+  int voff[4][2];         // per-lane LDS byte offsets of V transpose reads
 
-// One key tile for one wave: S^T = K Q^T, mask, online softmax update,
-// O^T = alpha * O^T + V^T P^T.
-template <int D, int DT, bool CAUSAL>
-__device__ __forceinline__ void consume_tile(WaveState<D>& st, const lds_t* Ks, const lds_t* Vs, int key0,
-                                             int qw0, int qrow, int diag, int Nk, int half, float c) {
-  constexpr int kRowBytes = D * 2;
-  constexpr int kKSteps = D / 16;
-  constexpr int kDBlocks = D / 32;
-
-  f32x16 s0 = {}, s1 = {};
+  __device__ __forceinline__ void init_offsets(int lane) {
+    constexpr int kRowBytes = D * 2;
+    const int half = lane >> 5, r32 = lane & 31;
+    // K operand: row r32 (+32 for the second key block), chunk 2s + half.
+    const int xk = swz<D>(r32);
 #pragma unroll
-  for (int s = 0; s < kKSteps; ++s) {
-    const int o = st.koff[s & 3] + (s >> 2) * 128;
-    const i16x8 a0 = *(const lds_i16x8*)(Ks + o);
-    const i16x8 a1 = *(const lds_i16x8*)(Ks + o + 32 * kRowBytes);
-    s0 = Elt<DT>::mma(a0, st.qf[s], s0);
-    s1 = Elt<DT>::mma(a1, st.qf[s], s1);
-  }
-
-  // Mask keys past Nk and (causal) above the diagonal; wave-uniform test.
-  const bool ragged = key0 + kBlockN > Nk;
-  const bool on_diag = CAUSAL && (key0 + kBlockN - 1 > qw0 + diag);
-  if (ragged || on_diag) {
-    const int lim = CAUSAL ? min(qrow + diag, Nk - 1) : Nk - 1;
+    for (int s = 0; s < kKOff; ++s) koff[s] = r32 * kRowBytes + (((2 * s + half) ^ xk) * 16);
+    // V transpose reads: 16-lane group G reads rows 4*(G>>1) + t/4 (+8 for
+    // the second read) and columns 16*(G&1) + 4*(t&3) of a 32-column block.
+    const int G = lane >> 4, t = lane & 15;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (key > lim) s0[r] = -__builtin_inff();
-      if (key + 32 > lim) s1[r] = -__builtin_inff();
+    for (int e = 0; e < 2; ++e) {
+      const int row = 4 * (G >> 1) + (t >> 2) + 8 * e;
+      const int x = swz<D>(row);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int chunk = (4 * db + 2 * (G & 1) + ((t & 3) >> 1)) ^ x;
+        voff[db][e] = row * kRowBytes + chunk * 16 + 8 * (t & 1);
+      }
     }
   }
+};
 
-  // Online softmax statistics for this lane's query row.
+// S^T = K Q^T for the 64 keys of one tile: two 32x32 accumulators.
+template <int D, int DT>
+__device__ __forceinline__ void tile_scores(const WaveState<D>& st, const lds_t* Ks, f32x16& s0, f32x16& s1) {
+  constexpr int kRowBytes = D * 2;
+  constexpr int kKOff = WaveState<D>::kKOff;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const int o = st.koff[s % kKOff] + (s / kKOff) * 256;
+    const i16x8 a0 = *(const lds_i16x8*)(Ks + o);
+    const i16x8 a1 = *(const lds_i16x8*)(Ks + o + 32 * kRowBytes);
+    s0 = Elt<DT>::mma(a0, st.qf[s], s == 0 ? f32x16{} : s0);
+    s1 = Elt<DT>::mma(a1, st.qf[s], s == 0 ? f32x16{} : s1);
+  }
+}
+
+// Rows may hold p = exp2(s*c - m2) up to 2^kLazy before the reference max
+// m2 is raised and O, l rescaled: the final O / l and m2 + log2 l do not
+// depend on which reference was used, only the rounding does.
+constexpr float kLazy = 8.0f;
+
+// Softmax of one tile's scores (s0, s1), ready for the P V product.
+struct SoftmaxOut {
+  i16x8 pf[4];   // P^T fragments: k-step ks covers keys 16ks..16ks+15 of the tile
+  float alpha;   // factor O and l must be multiplied by before adding this tile
+  bool rescale;  // wave-uniform: alpha != 1 for some lane
+};
+
+// Phase A of one pipelined step, a single branch-free block: the score
+// MFMAs of the NEXT tile (K from `Kn`) interleaved with the softmax of the
+// CURRENT tile (mask, row max, reference update, exp2, rounding of P).
+// sched_group_barrier lays the block out as [MFMA, ~7 VALU, K read] x 16 so
+// that the wave keeps issuing softmax VALU work while each MFMA runs.
+template <int D, int DT, bool MASK>
+__device__ __forceinline__ SoftmaxOut phase_a(WaveState<D>& st, f32x16 s0, f32x16 s1, const lds_t* Kn,
+                                              f32x16& n0, f32x16& n1, int rem, int half, float c) {
+  tile_scores<D, DT>(st, Kn, n0, n1);
+
+  if (MASK) {
+    // rem = last visible key of this lane's row minus the lane's first key
+    // (key0 + 4*half); element r of s0 sits 8*(r>>2) + (r&3) keys later, of
+    // s1 another 32.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int o = 8 * (r >> 2) + (r & 3);
+      s0[r] = o > rem ? -__builtin_inff() : s0[r];
+      s1[r] = o + 32 > rem ? -__builtin_inff() : s1[r];
+    }
+  }
   float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
   mx = swap_halves_max(mx);
-  const float m2new = fmaxf(st.m2, mx * c);
-  const float mref = (m2new == -__builtin_inff()) ? 0.f : m2new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m2 - mref);
+  const float m2t = mx * c;
+  SoftmaxOut out;
+  out.rescale = __any(m2t > st.m2 + kLazy);
+  const float m2new = out.rescale ? fmaxf(st.m2, m2t) : st.m2;
+  out.alpha = (m2new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(st.m2 - m2new);
   st.m2 = m2new;
-  float ls = 0.f;
+  const float mref = (m2new == -__builtin_inff()) ? 0.f : m2new;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, -mref));
     s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, -mref));
-    ls += s0[r] + s1[r];
   }
-  st.lrun = alpha * st.lrun + ls;
+  // row sum from the unrounded probabilities (kept in fp32)
+  float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-  for (int i = 0; i < kDBlocks; ++i) st.oacc[i] *= alpha;
-
-  // P^T fragments: k-step ks covers keys 16ks..16ks+15 of the tile.
-  i16x8 pf[4];
+  for (int r = 0; r < 16; ++r) {
+    ls0 += s0[r];
+    ls1 += s1[r];
+  }
+  st.lrun = out.alpha * st.lrun + (ls0 + ls1);
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
-    uint32_t w0[4], w1[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w0[i] = Elt<DT>::pack(s0[8 * hh + 2 * i], s0[8 * hh + 2 * i + 1]);
-      w1[i] = Elt<DT>::pack(s1[8 * hh + 2 * i], s1[8 * hh + 2 * i + 1]);
-    }
-    pf[hh] = __builtin_bit_cast(i16x8, u32x4{w0[0], w0[1], w0[2], w0[3]});
-    pf[2 + hh] = __builtin_bit_cast(i16x8, u32x4{w1[0], w1[1], w1[2], w1[3]});
+    out.pf[hh] = __builtin_bit_cast(i16x8, u32x4{Elt<DT>::pack(s0[8 * hh + 0], s0[8 * hh + 1]),
+                                                 Elt<DT>::pack(s0[8 * hh + 2], s0[8 * hh + 3]),
+                                                 Elt<DT>::pack(s0[8 * hh + 4], s0[8 * hh + 5]),
+                                                 Elt<DT>::pack(s0[8 * hh + 6], s0[8 * hh + 7])});
+    out.pf[2 + hh] = __builtin_bit_cast(i16x8, u32x4{Elt<DT>::pack(s1[8 * hh + 0], s1[8 * hh + 1]),
+                                                     Elt<DT>::pack(s1[8 * hh + 2], s1[8 * hh + 3]),
+                                                     Elt<DT>::pack(s1[8 * hh + 4], s1[8 * hh + 5]),
+                                                     Elt<DT>::pack(s1[8 * hh + 6], s1[8 * hh + 7])});
   }
+  // Interleave: 4 K reads up front, then [MFMA, 7 VALU, K read] x 16.
+  constexpr int kMfma = 2 * (D / 16);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < kMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    if (i + 4 < kMfma) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  return out;
+}
 
-  // O^T += V^T P^T.
+// Phase B: O^T = alpha * O^T + V^T P^T (the rescale is skipped when no lane
+// raised its reference max).
+template <int D, int DT>
+__device__ __forceinline__ void phase_b(WaveState<D>& st, const SoftmaxOut& sm, const lds_t* Vs) {
+  constexpr int kRowBytes = D * 2;
+  constexpr int kDBlocks = D / 32;
+  if (sm.rescale) {
+#pragma unroll
+    for (int i = 0; i < kDBlocks; ++i) st.oacc[i] *= sm.alpha;
+  }
 #pragma unroll
   for (int db = 0; db < kDBlocks; ++db) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const lds_t* base = Vs + st.voff[db & 1] + (db >> 1) * 128 + 16 * ks * kRowBytes;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)base);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * kRowBytes));
+      const lds_t* base = Vs + (db >> 2) * 256 + 16 * ks * kRowBytes;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + st.voff[db & 3][0]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + st.voff[db & 3][1]));
       const i16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      st.oacc[db] = Elt<DT>::mma(a, pf[ks], st.oacc[db]);
+      st.oacc[db] = Elt<DT>::mma(a, sm.pf[ks], st.oacc[db]);
     }
   }
+}
+
+// One pipelined step for tile j (scores in s0/s1): next tile's scores into
+// n0/n1 from Kn, softmax and P V of tile j with V from Vs.
+template <int D, int DT, bool CAUSAL>
+__device__ __forceinline__ void step(WaveState<D>& st, f32x16 s0, f32x16 s1, f32x16& n0, f32x16& n1,
+                                     const lds_t* Kn, const lds_t* Vs, int key0, int qw0, int qrow, int diag,
+                                     int Nk, int half, float c) {
+  const bool ragged = key0 + kBlockN > Nk;
+  const bool on_diag = CAUSAL && (key0 + kBlockN - 1 > qw0 + diag);
+  SoftmaxOut sm;
+  if (ragged || on_diag) {
+    const int lim = CAUSAL ? min(qrow + diag, Nk - 1) : Nk - 1;
+    sm = phase_a<D, DT, true>(st, s0, s1, Kn, n0, n1, lim - key0 - 4 * half, half, c);
+  } else {
+    sm = phase_a<D, DT, false>(st, s0, s1, Kn, n0, n1, 0, half, c);
+  }
+  phase_b<D, DT>(st, sm, Vs);
 }
 
 template <int D, int DT, bool CAUSAL>
@@ -252,17 +356,20 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(Params p) {
   constexpr int kTileBytes = kBlockN * kRowBytes;
   constexpr int kKSteps = D / 16;
   constexpr int kDBlocks = D / 32;
-  // The two ring stages are separate LDS objects and the key loop is
-  // unrolled by two, so every LDS read names its stage statically: the
-  // compiler can then prove that reads of one stage never alias the
-  // in-flight direct-to-LDS loads into the other and does not wait on them.
+  // K and V rings of two stages each, as four separate LDS objects.  K runs
+  // one tile ahead of V: while a wave applies the softmax of tile j it
+  // already multiplies K_{j+1} (the two-stage overlap of score MFMAs with
+  // softmax inside one wave).  With every stage a distinct object and the
+  // loop unrolled by two, each LDS read names its stage statically, so the
+  // compiler can prove it never aliases the in-flight direct-to-LDS loads
+  // into another stage and does not wait on them.
   __shared__ __attribute__((aligned(1024))) unsigned char k_st0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_st0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char k_st1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char v_st1[kTileBytes];
   lds_t* const K0 = (lds_t*)k_st0;
-  lds_t* const V0 = (lds_t*)v_st0;
   lds_t* const K1 = (lds_t*)k_st1;
+  lds_t* const V0 = (lds_t*)v_st0;
   lds_t* const V1 = (lds_t*)v_st1;
 
   const int lane = threadIdx.x & 63;
@@ -280,68 +387,58 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(Params p) {
   int kend = p.Nk;
   if (CAUSAL) kend = min(p.Nk, q0 + kBlockM + diag);
   const int nt = kend > 0 ? (kend + kBlockN - 1) / kBlockN : 0;
+  // Causal: tiles starting past this wave's last visible key contribute nothing.
+  const int wave_kend = CAUSAL ? qw0 + kRowsPerWave - 1 + diag : p.Nk;
 
   const uint16_t* Qb = p.q + (size_t)bh * p.Nq * D;
-  const uint16_t* Kb = p.k + (size_t)bh * p.Nk * D;
-  const uint16_t* Vb = p.v + (size_t)bh * p.Nk * D;
+  const uint32_t head_bytes = (uint32_t)p.Nk * kRowBytes;
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(p.k + (size_t)bh * p.Nk * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(p.v + (size_t)bh * p.Nk * D, head_bytes);
 
+  TileLoader<D> ld;
+  ld.init(wave, lane);
   WaveState<D> st;
+  st.init_offsets(lane);
   {
     const int row = min(qrow, p.Nq - 1);
     const i16x8* src = (const i16x8*)(Qb + (size_t)row * D);
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s) st.qf[s] = src[2 * s + half];
   }
-  // K operand: row r32 (+32 for the second key block), chunk 2s + half.
-  {
-    const int x = swz(r32);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) st.koff[s] = r32 * kRowBytes + (((2 * s + half) ^ x) * 16);
-  }
-  // V transpose reads: 16-lane group G reads rows 4*(G>>1) + t/4 and columns
-  // 16*(G&1) + 4*(t&3) of each 32-column block (t = lane & 15).
-  {
-    const int G = lane >> 4, t = lane & 15;
-    const int row = 4 * (G >> 1) + (t >> 2);
-    const int x = swz(row);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int chunk = 4 * e + 2 * (G & 1) + ((t & 3) >> 1);
-      st.voff[e] = row * kRowBytes + ((chunk ^ x) * 16) + 8 * (t & 1);
-    }
-  }
 #pragma unroll
   for (int i = 0; i < kDBlocks; ++i) st.oacc[i] = f32x16{};
   st.m2 = -__builtin_inff();
   st.lrun = 0.f;
 
-  // Causal: tiles entirely above this wave's diagonal contribute nothing.
-  const int wave_kend = qw0 + kRowsPerWave - 1 + diag;  // last key any row of the wave sees
-
+  // Scores of even tiles live in (a0, a1), of odd tiles in (b0, b1).  Each
+  // step computes the next tile's scores unconditionally (the K stage it
+  // reads always holds valid LDS; after the last tile the result is unused)
+  // so that the MFMAs share one branch-free block with the softmax.
+  f32x16 a0, a1, b0, b1;
   if (nt > 0) {
-    load_tile<D>(K0, Kb, 0, p.Nk, wave, lane);
-    load_tile<D>(V0, Vb, 0, p.Nk, wave, lane);
+    ld.load(K0, Kr, 0);
+    ld.load(V0, Vr, 0);
+    if (nt > 1) ld.load(K1, Kr, kBlockN);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    tile_scores<D, DT>(st, K0, a0, a1);
   }
   for (int j = 0; j < nt; j += 2) {
-    // stage 0 holds tile j; prefetch tile j+1 into stage 1
+    // Even step: (a0, a1) = scores of tile j; K_{j+1} is in K1, V_j in V0.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 1 < nt) {
-      load_tile<D>(K1, Kb, (j + 1) * kBlockN, p.Nk, wave, lane);
-      load_tile<D>(V1, Vb, (j + 1) * kBlockN, p.Nk, wave, lane);
-    }
-    if (!CAUSAL || j * kBlockN <= wave_kend)
-      consume_tile<D, DT, CAUSAL>(st, K0, V0, j * kBlockN, qw0, qrow, diag, p.Nk, half, p.c);
+    if (j + 2 < nt) ld.load(K0, Kr, (j + 2) * kBlockN);
+    if (j + 1 < nt) ld.load(V1, Vr, (j + 1) * kBlockN);
+    if (j * kBlockN <= wave_kend)
+      step<D, DT, CAUSAL>(st, a0, a1, b0, b1, K1, V0, j * kBlockN, qw0, qrow, diag, p.Nk, half, p.c);
     if (j + 1 >= nt) break;
-    // stage 1 holds tile j+1; prefetch tile j+2 into stage 0
+    // Odd step: (b0, b1) = scores of tile j+1; K_{j+2} is in K0, V_{j+1} in V1.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 2 < nt) {
-      load_tile<D>(K0, Kb, (j + 2) * kBlockN, p.Nk, wave, lane);
-      load_tile<D>(V0, Vb, (j + 2) * kBlockN, p.Nk, wave, lane);
-    }
-    if (!CAUSAL || (j + 1) * kBlockN <= wave_kend)
-      consume_tile<D, DT, CAUSAL>(st, K1, V1, (j + 1) * kBlockN, qw0, qrow, diag, p.Nk, half, p.c);
+    if (j + 3 < nt) ld.load(K1, Kr, (j + 3) * kBlockN);
+    if (j + 2 < nt) ld.load(V0, Vr, (j + 2) * kBlockN);
+    if ((j + 1) * kBlockN <= wave_kend)
+      step<D, DT, CAUSAL>(st, b0, b1, a0, a1, K0, V1, (j + 1) * kBlockN, qw0, qrow, diag, p.Nk, half, p.c);
   }
 
   // Epilogue: O = O^T / l, LSE = ln2 * (m2 + log2 l).
@@ -400,7 +497,22 @@ int launch_dtype(const Problem& p, hipStream_t s) {
   }
 }
 
-}  // namespace
+// Explicit instantiations: every kernel the dispatcher can launch, so the
+// host pass emits each launch stub.
+#define ATTN_INSTANTIATE(D, DT)                                                  \
+  template __global__ void attn_fwd_kernel<D, DT, false>(Params);               \
+  template __global__ void attn_fwd_kernel<D, DT, true>(Params);
+ATTN_INSTANTIATE(64, ATTN_F16)
+ATTN_INSTANTIATE(128, ATTN_F16)
+ATTN_INSTANTIATE(256, ATTN_F16)
+ATTN_INSTANTIATE(64, ATTN_BF16)
+ATTN_INSTANTIATE(128, ATTN_BF16)
+ATTN_INSTANTIATE(256, ATTN_BF16)
+#undef ATTN_INSTANTIATE
+
+}  // namespace kernels
+
+using namespace kernels;
 
 int launch_forward(const Problem& p, hipStream_t stream) {
   switch (p.dtype) {

@@ -76,6 +76,27 @@ def _cpu_baseline(inp, budget_s):
     }
 
 
+def _copy_calibration(torch, args):
+    """A plain copy kernel moving a known byte count (read n, write n): the
+    FETCH_SIZE / WRITE_SIZE counters it reads calibrate the HBM traffic of
+    the attention kernel."""
+    n = args.copy_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms, "GB/s": 2 * n / ms / 1e6}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,6 +105,8 @@ def main():
     ap.add_argument("--workload", default="hd128_seq8k_f16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of attention, time a plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -92,6 +115,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_mib:
+        _copy_calibration(torch, args)
+        return
     from attention_forward_02_amd import inputs
     from attention_forward_02_amd.binding import attn_fwd, attn_fwd_fp8, ATTN_F16, ATTN_BF16, ATTN_OK, AttnError
 

@@ -1,20 +1,49 @@
 """Build libattn.so (the C-ABI HIP library) in-tree with hipcc for gfx950.
 
 Usage: python -m attention_forward_02_amd.build [-v]
+
+Each source compiles to its own object (in parallel), then hipcc links the
+shared library.  The kernels of each head dimension are a translation unit
+of their own so that each gets the register-form options that suit it.
 """
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.cpp", "attn_fwd.hip"]
 ARCH = "gfx950"
+
+COMMON = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    # Packed FP32 VALU forms stay off: hipcc would otherwise emit them from
+    # ordinary float2 arithmetic.  The host pass ignores the flag.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+    # No NaN-quieting copies around fmaxf in the row-max reductions.
+    "-fno-honor-nans",
+]
+# MFMA accumulators in ordinary VGPRs: the softmax reads and rescales them
+# every tile, and AGPR-resident accumulators would need copies.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+
+SOURCES = [
+    ("attn_api.cpp", []),
+    ("attn_dispatch.cpp", []),
+    ("attn_fwd_d64.hip", VGPR_FORM),
+    ("attn_fwd_d128.hip", VGPR_FORM),
+    ("attn_fwd_d256.hip", VGPR_FORM),
+]
 
 
 def hipcc():
@@ -24,44 +53,35 @@ def hipcc():
     raise RuntimeError("hipcc not found; set ROCM_PATH")
 
 
-def command(out=LIB):
-    return [
-        hipcc(),
-        f"--offload-arch={ARCH}",
-        "-O3",
-        "-std=c++17",
-        "-fPIC",
-        "-shared",
-        # Packed FP32 VALU forms stay off: hipcc would otherwise emit them
-        # from ordinary float2 arithmetic.  The host pass ignores the flag.
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wno-unused-command-line-argument",
-        # MFMA accumulators in ordinary VGPRs: the softmax rescales them
-        # every tile, and AGPR-resident accumulators would need copies.
-        "-mllvm", "-amdgpu-mfma-vgpr-form",
-        # No NaN-quieting copies around fmaxf in the row-max reductions.
-        "-fno-honor-nans",
-        "-I", INCLUDE,
-        "-I", CSRC,
-        *[os.path.join(CSRC, s) for s in SOURCES],
-        "-o", out,
-    ]
+def compile_command(src, extra, obj):
+    return [hipcc(), *COMMON, *extra, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
 
 
-def build(verbose=False):
-    """Compile every source into libattn.so next to this file (always
-    recompiles) and return its path."""
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    if verbose and res.stderr.strip():
-        sys.stderr.write(res.stderr)
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}: {' '.join(cmd)}")
+    return res
+
+
+def build(verbose=False):
+    """Compile every source and link libattn.so next to this file (always
+    recompiles) and return its path."""
+    with tempfile.TemporaryDirectory(prefix="attn_build_") as tmp:
+        objs, cmds = [], []
+        for src, extra in SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            objs.append(obj)
+            cmds.append(compile_command(src, extra, obj))
+        workers = min(len(cmds), max(1, (os.cpu_count() or 2)))
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        out = LIB + ".tmp"
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out], verbose)
+        os.replace(out, LIB)
     return LIB
 
 

@@ -10,6 +10,8 @@ template __global__ void attn_fwd_kernel<64, ATTN_F16, false>(Params);
 template __global__ void attn_fwd_kernel<64, ATTN_F16, true>(Params);
 template __global__ void attn_fwd_kernel<64, ATTN_BF16, false>(Params);
 template __global__ void attn_fwd_kernel<64, ATTN_BF16, true>(Params);
+template __global__ void attn_fwd_kernel<64, ATTN_FP8_E4M3, false>(Params);
+template __global__ void attn_fwd_kernel<64, ATTN_FP8_E4M3, true>(Params);
 
 }  // namespace kernels
 

@@ -17,12 +17,14 @@
 //     stage.  The 16-byte chunks of a row are XOR-swizzled so MFMA operand
 //     reads spread over the 64 LDS banks.
 //   * Scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_{f16,bf16}: the accumulator then gives every lane
-//     32 scores of ONE query row (lanes l and l+32 share a row), so the row
-//     max and row sum are in-lane work plus one v_permlane32_swap.
+//     v_mfma_f32_32x32x16_{f16,bf16} (or v_mfma_f32_32x32x64_f8f6f4 for
+//     E4M3): the accumulator then gives every lane 32 scores of ONE query
+//     row (lanes l and l+32 share a row), so the row max and row sum are
+//     in-lane work plus one v_permlane32_swap.
 //   * The output is accumulated transposed too, O^T += V^T P^T: P^T is the
 //     score accumulator itself after exp2 and rounding (no data movement),
-//     and V^T comes from LDS through ds_read_b64_tr_b16 transpose reads.
+//     and V^T comes from LDS through ds_read_b64_tr_b16 / ds_read_b64_tr_b8
+//     transpose reads.
 //   * exp is v_exp_f32 (2^x) on scores pre-multiplied by scale * log2(e);
 //     LSE is converted back to natural log at the end.
 //
@@ -30,11 +32,16 @@
 // d <= 128 so that every SIMD runs two waves): each step overlaps the score
 // MFMAs of the next tile with the exponentials of the current one, and the
 // P V MFMAs with the row sums and the next tile's row max (the pages'
-// two-stage overlap of matrix multiplies and softmax), so a wave issues
-// only about five VALU instructions per MFMA and the matrix core stays fed
-// from both waves of the SIMD.  Masking is folded into the initial values
-// of the score accumulators, so the step is the same branch-free code for
-// every tile.
+// two-stage overlap of matrix multiplies and softmax), so the matrix core
+// stays fed from both waves of the SIMD.  Masking is folded into the
+// initial values of the score accumulators, so the step is the same
+// branch-free code for every tile.
+//
+// FP8 E4M3 ("Inside FlashAttention-3", section 5): Q, K, V are E4M3 codes
+// with one descale per tensor.  The q and k descales are folded into the
+// score scale and the v descale into the final normalisation; P is rounded
+// to E4M3 (round to nearest even) for the P V product while the row sum
+// uses the unrounded probabilities; O is binary16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -53,6 +60,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -63,61 +73,113 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) i16x8 lds_i16x8;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 
 struct Params {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
+  const unsigned char* q;
+  const unsigned char* k;
+  const unsigned char* v;
   uint16_t* o;
   float* lse;
   int Nq, Nk;
   int n_qtiles;     // ceil(Nq / query rows per workgroup)
   int total_tiles;  // B * H * n_qtiles
   float c;          // scale * log2(e): scores -> base-2 exponent units
+  float o_scale;    // multiplies P V (the v descale for E4M3, else 1)
 };
 
-// 16-bit element types: MFMA and float -> element rounding (RNE).
+// Input element formats: size and MFMA.
 template <int DT>
-struct Elt;
+struct Fmt;
 
 template <>
-struct Elt<ATTN_F16> {
+struct Fmt<ATTN_F16> {
+  static constexpr int kBytes = 2;
   static __device__ __forceinline__ f32x16 mma(i16x8 a, i16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t pack(float x, float y) {  // v_cvt_pk_f16_f32 (RNE)
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, f16x2));
-  }
 };
 
 template <>
-struct Elt<ATTN_BF16> {
+struct Fmt<ATTN_BF16> {
+  static constexpr int kBytes = 2;
   static __device__ __forceinline__ f32x16 mma(i16x8 a, i16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t pack(float x, float y) {  // v_cvt_pk_bf16_f32 (RNE)
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
+};
+
+template <>
+struct Fmt<ATTN_FP8_E4M3> {
+  static constexpr int kBytes = 1;
+  // v_mfma_f32_32x32x64_f8f6f4 with both operands E4M3 (format code 0) and
+  // no block scales.
+  static __device__ __forceinline__ f32x16 mma(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
   }
 };
 
-// XOR swizzle of the 16-byte chunk index within a row.  The gfx950 LDS
-// serves 256 bytes (64 banks x 4 B) per cycle, i.e. 16 lanes of a 128-bit
-// read or 32 lanes of a 64-bit read.  Two access patterns must be
-// conflict-free:
-//   * K operand reads (ds_read_b128): 16 consecutive rows, one logical chunk;
+// Float pairs -> packed 16-bit output / probability elements (RNE):
+// binary16 for f16 and E4M3 inputs, bfloat16 for bf16 inputs.
+template <int DT>
+__device__ __forceinline__ uint32_t pack16(float x, float y) {
+  if constexpr (DT == ATTN_BF16)  // v_cvt_pk_bf16_f32
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
+  else  // v_cvt_pk_f16_f32
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, f16x2));
+}
+
+// Four floats -> four E4M3 bytes, in order (v_cvt_pk_fp8_f32 twice, RNE).
+// Inputs here are probabilities in [0, 2^8], inside E4M3's finite range.
+__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// XOR swizzle f(row) of the 16-byte chunk index within an LDS row: logical
+// chunk c of row r sits at chunk c ^ f(r).  The gfx950 LDS serves 256 bytes
+// (64 banks x 4 B) per cycle, i.e. 16 lanes of a 128-bit read or 32 lanes of
+// a 64-bit read, and each format's operand reads must fill those 256 bytes
+// without two lanes meeting in one bank:
+//
+// 16-bit elements (row bytes 2d):
+//   * K reads (ds_read_b128): 16 consecutive rows, one logical chunk;
 //   * V transpose reads (ds_read_b64_tr_b16): 4 consecutive rows (a 4-aligned
 //     group) x 4 consecutive chunks (a 4-aligned group).
-// Rows of >= 256 bytes (d >= 128): f(r) = 4*(r&3) + ((r>>2)&3) is a bijection
-// on r mod 16, and inside a 4-row group its values differ in bits [3:2].
-// Rows of 128 bytes (d = 64) put two rows in one 256-byte bank window: f(r)
-// = 4*((r>>1)&1) + ((r>>2)&3) is distinct over the even and over the odd
-// rows of any 16, and rows r, r+2 of a 4-row group differ in bit 2.
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-  else return ((row & 2) << 1) | ((row >> 2) & 3);
+//   Rows of >= 256 bytes: f(r) = 4*(r&3) + ((r>>2)&3) is a bijection on
+//   r mod 16, and inside a 4-row group its values differ in bits [3:2].
+//   Rows of 128 bytes (two rows per bank window): f(r) = 4*((r>>1)&1) +
+//   ((r>>2)&3) is distinct over the even and over the odd rows of any 16,
+//   and rows r, r+2 of a 4-row group differ in bit 2.
+//
+// E4M3 elements (row bytes d):
+//   * K reads (ds_read_b128): as above;
+//   * V transpose reads (ds_read_b64_tr_b8): rows {b..b+3, b+8..b+11}
+//     (b = 0 or 4 mod 16) x one aligned pair of chunks {2m, 2m+1}.
+//   With (r0, r1, r2, r3) the low bits of the row:
+//   256-byte rows: f = (r3, r1, r0, r2) as bits [3:0] -- a bijection on
+//     r mod 16, and f >> 1 = (r3, r1, r0) is distinct over the 8 rows of a
+//     transpose read;
+//   128-byte rows (two rows per window, r0 selects the half): f = (r3, r1,
+//     r2) as bits [2:0] -- distinct over the rows of one parity, and f >> 1 =
+//     (r3, r1) distinct over the 4 rows of one parity in a transpose read;
+//   64-byte rows (four rows per window, r1:r0 selects the quarter): f =
+//     (r3, r2) as bits [1:0] -- distinct over 4 rows of one residue, and the
+//     2 rows of one residue in a transpose read differ in r3.
+// Every f uses bits [3:0] of the row only, so f(r + 16k) = f(r).
+template <int D, int DT>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (Fmt<DT>::kBytes == 2) {
+    if constexpr (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return ((r & 2) << 1) | ((r >> 2) & 3);
+  } else {
+    const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+    if constexpr (D == 256) return (r3 << 3) | (r1 << 2) | (r0 << 1) | r2;
+    else if constexpr (D == 128) return (r3 << 2) | (r1 << 1) | r2;
+    else return (r3 << 1) | r2;
+  }
 }
 
 __device__ __forceinline__ float swap_halves_max(float x) {
@@ -155,10 +217,10 @@ __device__ __forceinline__ void schedule(const Params& p, int bid, bool causal, 
 // so rows past Nk (a ragged last tile) fail the hardware range check and
 // arrive as zeros; their scores are masked to -inf and their zero values
 // meet P = 0.
-template <int D, int NW>
+template <int D, int DT, int NW>
 struct TileLoader {
-  static constexpr int kRowBytes = D * 2;
-  static constexpr int kChunks = D / 8;
+  static constexpr int kRowBytes = D * Fmt<DT>::kBytes;
+  static constexpr int kChunks = kRowBytes / 16;
   static constexpr int kRowsPerKB = 1024 / kRowBytes;
   static constexpr int kBlocks = kBlockN * kRowBytes / 1024;
   static constexpr int kPerWave = kBlocks / NW;
@@ -171,7 +233,7 @@ struct TileLoader {
     for (int i = 0; i < kPerWave; ++i) {
       const int b = i * NW + wave;
       const int row = b * kRowsPerKB + lane / kChunks;
-      voff[i] = row * kRowBytes + ((lane % kChunks) ^ swz<D>(row)) * 16;
+      voff[i] = row * kRowBytes + ((lane % kChunks) ^ swz<D, DT>(row)) * 16;
       lds[i] = b * 1024;
     }
   }
@@ -189,9 +251,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
 }
 
-// Per-wave state carried across key tiles.
-template <int D>
-struct WaveState {
+// Per-wave state carried across key tiles, 16-bit inputs.
+//   MFMA 32x32x16: lane l holds row/column (l & 31) and k elements
+//   8*(l >> 5) .. +7 of each operand.
+template <int D, int DT>
+struct WaveState16 {
+  static constexpr int kRowBytes = D * 2;
   static constexpr int kKOff = (D / 16 < 8) ? D / 16 : 8;
   i16x8 qf[D / 16];       // Q rows of this lane as MFMA B-operand fragments
   f32x16 oacc[D / 32];    // O^T accumulator, 32 output columns per block
@@ -200,11 +265,10 @@ struct WaveState {
   int koff[kKOff];        // per-lane LDS byte offsets of K operand reads
   int voff[4][2];         // per-lane LDS byte offsets of V transpose reads
 
-  __device__ __forceinline__ void init(const uint16_t* Qb, int qrow, int Nq, int lane) {
-    constexpr int kRowBytes = D * 2;
+  __device__ __forceinline__ void init(const unsigned char* Qb, int qrow, int Nq, int lane) {
     const int half = lane >> 5, r32 = lane & 31;
     // Q rows of this lane: chunk (2s + half) of the row, clamped for rows past Nq.
-    const i16x8* src = (const i16x8*)(Qb + (size_t)min(qrow, Nq - 1) * D);
+    const i16x8* src = (const i16x8*)(Qb + (size_t)min(qrow, Nq - 1) * kRowBytes);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qf[s] = src[2 * s + half];
 #pragma unroll
@@ -212,7 +276,7 @@ struct WaveState {
     m2 = -__builtin_inff();
     lrun = 0.f;
     // K operand: row r32 (+32 for the second key block), chunk 2s + half.
-    const int xk = swz<D>(r32);
+    const int xk = swz<D, DT>(r32);
 #pragma unroll
     for (int s = 0; s < kKOff; ++s) koff[s] = r32 * kRowBytes + (((2 * s + half) ^ xk) * 16);
     // V transpose reads: 16-lane group G reads rows 4*(G>>1) + t/4 (+8 for
@@ -221,7 +285,7 @@ struct WaveState {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int row = 4 * (G >> 1) + (t >> 2) + 8 * e;
-      const int x = swz<D>(row);
+      const int x = swz<D, DT>(row);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int chunk = (4 * db + 2 * (G & 1) + ((t & 3) >> 1)) ^ x;
@@ -231,26 +295,104 @@ struct WaveState {
   }
 };
 
+// Per-wave state, E4M3 inputs.
+//   MFMA 32x32x64 f8: lane l holds row/column (l & 31) and the 32
+//   consecutive k elements 32*(l >> 5) .. +31 of each operand.
+//   Scores: MFMA k-step s covers head-dim bytes 64s .. 64s+63.
+//   P V: the 64 keys of a tile are the MFMA's k, in the order of the score
+//   accumulator: the lane's 32-byte B operand holds P for keys
+//   32s + 8i + 4h + j at byte 16s + 4i + j (h = lane half; i, j < 4), so the
+//   A operand (V^T) is read in that key order.
+template <int D>
+struct WaveState8 {
+  static constexpr int kRowBytes = D;
+  i32x8 qf[D / 64];       // Q rows of this lane as MFMA B-operand fragments
+  f32x16 oacc[D / 32];    // O^T accumulator, 32 output columns per block
+  float m2;               // reference row max for exp2, in units of c
+  float lrun;             // running row sum over this lane's half of the keys
+  int koff[D / 32];       // K operand reads: two 16-byte chunks per k-step
+  int voff[D / 32];       // V transpose reads: one offset per 32-column block
+
+  __device__ __forceinline__ void init(const unsigned char* Qb, int qrow, int Nq, int lane) {
+    const int half = lane >> 5, r32 = lane & 31;
+    const i32x4* src = (const i32x4*)(Qb + (size_t)min(qrow, Nq - 1) * kRowBytes);
+#pragma unroll
+    for (int s = 0; s < D / 64; ++s) {
+      const i32x4 lo = src[4 * s + 2 * half], hi = src[4 * s + 2 * half + 1];
+      qf[s] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+    m2 = -__builtin_inff();
+    lrun = 0.f;
+    // K operand: row r32 (+32 for the second key block), chunks 4s + 2*half + e.
+    const int xk = swz<D, ATTN_FP8_E4M3>(r32);
+#pragma unroll
+    for (int s = 0; s < D / 64; ++s)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) koff[2 * s + e] = r32 * kRowBytes + (((4 * s + 2 * half + e) ^ xk) * 16);
+    // V transpose reads (ds_read_b64_tr_b8): in a 16-lane group G, result
+    // byte t of lane i is byte (i & 7) of the 8 bytes addressed by lane
+    // 2t + (i >> 3).  Read e (0..3) must give lane i the keys of bytes
+    // 8e..8e+7 of the k order above -- keys 16e + 4h + 8*(t>>2) + (t&3) --
+    // for head-dim column 32*db + 16*(G&1) + i.  So lane p addresses row
+    // 16e + 4h + 8*(p>>3) + ((p>>1)&3), columns 32*db + 16*(G&1) + 8*(p&1) .. +7;
+    // the 16e part is a constant offset of each read.
+    const int G = lane >> 4, p = lane & 15;
+    const int row = 4 * half + 8 * (p >> 3) + ((p >> 1) & 3);
+    const int xv = swz<D, ATTN_FP8_E4M3>(row);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      voff[db] = row * kRowBytes + (((2 * db + (G & 1)) ^ xv) * 16) + 8 * (p & 1);
+  }
+};
+
+template <int D, int DT>
+struct StateOf {
+  typedef WaveState16<D, DT> type;
+};
+template <int D>
+struct StateOf<D, ATTN_FP8_E4M3> {
+  typedef WaveState8<D> type;
+};
+template <int D, int DT>
+using WaveState = typename StateOf<D, DT>::type;
+
 // S^T = K Q^T for the 64 keys of one tile: two 32x32 accumulators.  With
 // BIAS the accumulators start from their current contents (a 0 / -inf mask
 // bias, see score_bias) instead of zero.
 template <int D, int DT, bool BIAS = false>
-__device__ __forceinline__ void tile_scores(const WaveState<D>& st, const lds_t* Ks, f32x16& s0, f32x16& s1) {
+__device__ __forceinline__ void tile_scores(const WaveState16<D, DT>& st, const lds_t* Ks, f32x16& s0, f32x16& s1) {
   constexpr int kRowBytes = D * 2;
-  constexpr int kKOff = WaveState<D>::kKOff;
+  constexpr int kKOff = WaveState16<D, DT>::kKOff;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     const int o = st.koff[s % kKOff] + (s / kKOff) * 256;
     const i16x8 a0 = *(const lds_i16x8*)(Ks + o);
     const i16x8 a1 = *(const lds_i16x8*)(Ks + o + 32 * kRowBytes);
-    s0 = Elt<DT>::mma(a0, st.qf[s], (s == 0 && !BIAS) ? f32x16{} : s0);
-    s1 = Elt<DT>::mma(a1, st.qf[s], (s == 0 && !BIAS) ? f32x16{} : s1);
+    s0 = Fmt<DT>::mma(a0, st.qf[s], (s == 0 && !BIAS) ? f32x16{} : s0);
+    s1 = Fmt<DT>::mma(a1, st.qf[s], (s == 0 && !BIAS) ? f32x16{} : s1);
+  }
+}
+
+template <int D, int DT, bool BIAS = false>
+__device__ __forceinline__ void tile_scores(const WaveState8<D>& st, const lds_t* Ks, f32x16& s0, f32x16& s1) {
+  constexpr int kRowBytes = D;
+#pragma unroll
+  for (int s = 0; s < D / 64; ++s) {
+    const lds_t* k0 = Ks + st.koff[2 * s];
+    const lds_t* k1 = Ks + st.koff[2 * s + 1];
+    const i32x8 a0 = __builtin_shufflevector(*(const lds_i32x4*)k0, *(const lds_i32x4*)k1, 0, 1, 2, 3, 4, 5, 6, 7);
+    const i32x8 a1 = __builtin_shufflevector(*(const lds_i32x4*)(k0 + 32 * kRowBytes),
+                                             *(const lds_i32x4*)(k1 + 32 * kRowBytes), 0, 1, 2, 3, 4, 5, 6, 7);
+    s0 = Fmt<ATTN_FP8_E4M3>::mma(a0, st.qf[s], (s == 0 && !BIAS) ? f32x16{} : s0);
+    s1 = Fmt<ATTN_FP8_E4M3>::mma(a1, st.qf[s], (s == 0 && !BIAS) ? f32x16{} : s1);
   }
 }
 
 // O^T += V^T P^T for one tile, V from LDS through transpose reads.
 template <int D, int DT>
-__device__ __forceinline__ void pv_tile(WaveState<D>& st, const i16x8 (&pf)[4], const lds_t* Vs) {
+__device__ __forceinline__ void pv_tile(WaveState16<D, DT>& st, const i16x8 (&pf)[4], const lds_t* Vs) {
   constexpr int kRowBytes = D * 2;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
@@ -260,14 +402,32 @@ __device__ __forceinline__ void pv_tile(WaveState<D>& st, const i16x8 (&pf)[4], 
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + st.voff[db & 3][0]));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + st.voff[db & 3][1]));
       const i16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      st.oacc[db] = Elt<DT>::mma(a, pf[ks], st.oacc[db]);
+      st.oacc[db] = Fmt<DT>::mma(a, pf[ks], st.oacc[db]);
     }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void pv_tile(WaveState8<D>& st, const i32x8& pf, const lds_t* Vs) {
+  constexpr int kRowBytes = D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const lds_t* base = Vs + st.voff[db];
+    const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(base));
+    const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(base + 16 * kRowBytes));
+    const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(base + 32 * kRowBytes));
+    const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(base + 48 * kRowBytes));
+    const i32x4 lo = __builtin_shufflevector(r0, r1, 0, 1, 2, 3);
+    const i32x4 hi = __builtin_shufflevector(r2, r3, 0, 1, 2, 3);
+    const i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    st.oacc[db] = Fmt<ATTN_FP8_E4M3>::mma(a, pf, st.oacc[db]);
   }
 }
 
 // Rows may hold p = exp2(s*c - m2) up to 2^kLazy before the reference max
 // m2 is raised and O, l rescaled: the final O / l and m2 + log2 l do not
-// depend on which reference was used, only the rounding does.
+// depend on which reference was used, only the rounding does.  (2^8 also
+// keeps every E4M3-rounded probability inside that format's range.)
 constexpr float kLazy = 8.0f;
 
 // Mask bias of a tile: rem = last visible key of this lane's row minus the
@@ -296,10 +456,20 @@ __device__ __forceinline__ float tile_max2(const f32x16& s0, const f32x16& s1, f
 
 template <int DT>
 __device__ __forceinline__ i16x8 pack8(const f32x16& p, int base) {
-  return __builtin_bit_cast(i16x8, u32x4{Elt<DT>::pack(p[base + 0], p[base + 1]),
-                                         Elt<DT>::pack(p[base + 2], p[base + 3]),
-                                         Elt<DT>::pack(p[base + 4], p[base + 5]),
-                                         Elt<DT>::pack(p[base + 6], p[base + 7])});
+  return __builtin_bit_cast(i16x8, u32x4{pack16<DT>(p[base + 0], p[base + 1]), pack16<DT>(p[base + 2], p[base + 3]),
+                                         pack16<DT>(p[base + 4], p[base + 5]), pack16<DT>(p[base + 6], p[base + 7])});
+}
+
+// P^T as the E4M3 B operand of the P V MFMA: byte 16s + r holds element r
+// of the tile's s-th score accumulator.
+__device__ __forceinline__ i32x8 pack_p_fp8(const f32x16& p0, const f32x16& p1) {
+  i32x8 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    r[w] = pack_fp8x4(p0[4 * w], p0[4 * w + 1], p0[4 * w + 2], p0[4 * w + 3]);
+    r[w + 4] = pack_fp8x4(p1[4 * w], p1[4 * w + 1], p1[4 * w + 2], p1[4 * w + 3]);
+  }
+  return r;
 }
 
 // Per-wave constants of the key loop.
@@ -337,8 +507,8 @@ __device__ __forceinline__ bool score_bias(const LoopCtx& cx, int t, f32x16& s0,
 
 // Scores of tile t (K from Ks) into (s0, s1), masked through the bias.
 template <int D, int DT, bool CAUSAL>
-__device__ __forceinline__ void masked_scores(const WaveState<D>& st, const LoopCtx& cx, int t, const lds_t* Ks,
-                                              f32x16& s0, f32x16& s1) {
+__device__ __forceinline__ void masked_scores(const WaveState<D, DT>& st, const LoopCtx& cx, int t,
+                                              const lds_t* Ks, f32x16& s0, f32x16& s1) {
   if (score_bias<CAUSAL>(cx, t, s0, s1)) tile_scores<D, DT, true>(st, Ks, s0, s1);
   else tile_scores<D, DT, false>(st, Ks, s0, s1);
 }
@@ -354,9 +524,21 @@ __device__ __forceinline__ float update_reference(float& m2, float m2t, bool& re
   return alpha;
 }
 
+// Instruction interleave of one phase: after `pre` LDS reads, `n` groups of
+// one MFMA, `valu` VALU instructions and `reads` LDS reads.
+#define ATTN_INTERLEAVE(pre, n, valu, reads)                  \
+  do {                                                        \
+    __builtin_amdgcn_sched_group_barrier(0x100, pre, 0);      \
+    _Pragma("unroll") for (int i_ = 0; i_ < (n); ++i_) {      \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      \
+      __builtin_amdgcn_sched_group_barrier(0x002, valu, 0);   \
+      __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);  \
+    }                                                         \
+    __builtin_amdgcn_sched_barrier(0);                        \
+  } while (0)
+
 // One step of the key loop for tile j, as two MFMA blocks with the softmax
-// VALU work spread over both (about 5 VALU instructions per MFMA, which a
-// wave issues while its MFMAs run):
+// VALU work spread over both:
 //   phase A: S_{j+1} = K_{j+1} Q^T (Kn; into n0, n1)  | p_j = exp2(s_j*c - m2),
 //                                                         P_j = round(p_j)
 //   phase B: O^T += V_j^T P_j^T (Vs)                  | l += sum(p_j),
@@ -365,7 +547,7 @@ __device__ __forceinline__ float update_reference(float& m2, float m2t, bool& re
 // then, rarely, O and l are rescaled to the new reference.  s0, s1 hold S_j
 // on entry (and p_j after phase A).
 template <int D, int DT, bool CAUSAL>
-__device__ __forceinline__ void step(WaveState<D>& st, const LoopCtx& cx, int j, f32x16& s0, f32x16& s1,
+__device__ __forceinline__ void step(WaveState<D, DT>& st, const LoopCtx& cx, int j, f32x16& s0, f32x16& s1,
                                      f32x16& n0, f32x16& n1, const lds_t* Kn, const lds_t* Vs) {
   // Phase A
   masked_scores<D, DT, CAUSAL>(st, cx, j + 1, Kn, n0, n1);
@@ -375,21 +557,24 @@ __device__ __forceinline__ void step(WaveState<D>& st, const LoopCtx& cx, int j,
     s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cx.c, -mref));
     s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cx.c, -mref));
   }
-  i16x8 pf[4];
-  pf[0] = pack8<DT>(s0, 0);
-  pf[1] = pack8<DT>(s0, 8);
-  pf[2] = pack8<DT>(s1, 0);
-  pf[3] = pack8<DT>(s1, 8);
-  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-#pragma unroll
-  for (int i = 0; i < D / 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  if constexpr (DT == ATTN_FP8_E4M3) {
+    // D/32 MFMAs of 64 cycles per phase; two 16-byte K reads per MFMA.
+    const i32x8 pf = pack_p_fp8(s0, s1);
+    if constexpr (D == 64) ATTN_INTERLEAVE(2, 2, 40, 2);
+    else if constexpr (D == 128) ATTN_INTERLEAVE(2, 4, 20, 2);
+    else ATTN_INTERLEAVE(2, 8, 10, 2);
+    // Phase B
+    pv_tile<D>(st, pf, Vs);
+  } else {
+    i16x8 pf[4];
+    pf[0] = pack8<DT>(s0, 0);
+    pf[1] = pack8<DT>(s0, 8);
+    pf[2] = pack8<DT>(s1, 0);
+    pf[3] = pack8<DT>(s1, 8);
+    ATTN_INTERLEAVE(3, D / 8, 5, 1);
+    // Phase B
+    pv_tile<D, DT>(st, pf, Vs);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  // Phase B
-  pv_tile<D, DT>(st, pf, Vs);
   float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -399,14 +584,14 @@ __device__ __forceinline__ void step(WaveState<D>& st, const LoopCtx& cx, int j,
   st.lrun += ls0 + ls1;
   bool rescale;
   const float alpha = update_reference(st.m2, tile_max2(n0, n1, cx.c), rescale);
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-  for (int i = 0; i < D / 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  if constexpr (DT == ATTN_FP8_E4M3) {
+    // D/32 MFMAs, four 8-byte transpose reads each.
+    if constexpr (D == 64) ATTN_INTERLEAVE(4, 2, 30, 4);
+    else if constexpr (D == 128) ATTN_INTERLEAVE(4, 4, 15, 4);
+    else ATTN_INTERLEAVE(4, 8, 8, 4);
+  } else {
+    ATTN_INTERLEAVE(4, D / 8, 4, 2);
   }
-  __builtin_amdgcn_sched_barrier(0);
   if (rescale) {
     st.lrun *= alpha;
 #pragma unroll
@@ -414,13 +599,14 @@ __device__ __forceinline__ void step(WaveState<D>& st, const LoopCtx& cx, int j,
   }
 }
 
-// Output: O = O^T / l (rounded to the element type), LSE = ln2 * (m2 + log2 l).
+// Output: O = o_scale * O^T / l (rounded to the output type),
+// LSE = ln2 * (m2 + log2 l).
 template <int D, int DT>
-__device__ __forceinline__ void store_output(const Params& p, const WaveState<D>& st, int bh, int qrow,
+__device__ __forceinline__ void store_output(const Params& p, const WaveState<D, DT>& st, int bh, int qrow,
                                              int half) {
   const float ltot = swap_halves_sum(st.lrun);
   const bool has_key = ltot > 0.f;
-  const float inv = has_key ? 1.0f / ltot : 0.f;
+  const float inv = has_key ? p.o_scale / ltot : 0.f;
   if (qrow < p.Nq) {
     const size_t row = (size_t)bh * p.Nq + qrow;
     if (half == 0) p.lse[row] = has_key ? (st.m2 + __builtin_amdgcn_logf(ltot)) * kLn2 : -__builtin_inff();
@@ -431,8 +617,8 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<D>
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * db + 8 * g + 4 * half;
         u32x2 w;
-        w[0] = Elt<DT>::pack(st.oacc[db][4 * g] * inv, st.oacc[db][4 * g + 1] * inv);
-        w[1] = Elt<DT>::pack(st.oacc[db][4 * g + 2] * inv, st.oacc[db][4 * g + 3] * inv);
+        w[0] = pack16<DT>(st.oacc[db][4 * g] * inv, st.oacc[db][4 * g + 1] * inv);
+        w[1] = pack16<DT>(st.oacc[db][4 * g + 2] * inv, st.oacc[db][4 * g + 3] * inv);
         *(u32x2*)(orow + d0) = w;
       }
     }
@@ -444,7 +630,7 @@ constexpr int kBlockM = kWaves * kRowsPerWave;  // query rows per workgroup
 
 template <int D, int DT, bool CAUSAL>
 __global__ void __launch_bounds__(64 * kWaves) attn_fwd_kernel(Params p) {
-  constexpr int kRowBytes = D * 2;
+  constexpr int kRowBytes = D * Fmt<DT>::kBytes;
   constexpr int kTileBytes = kBlockN * kRowBytes;
   // K and V rings of two stages each, as four separate LDS objects.  K runs
   // one tile ahead of V: step j reads K_{j+1} (scores of the next tile) and
@@ -481,13 +667,13 @@ __global__ void __launch_bounds__(64 * kWaves) attn_fwd_kernel(Params p) {
   cx.nt = nt;
 
   const uint32_t head_bytes = (uint32_t)p.Nk * kRowBytes;
-  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(p.k + (size_t)bh * p.Nk * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(p.v + (size_t)bh * p.Nk * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(p.k + (size_t)bh * p.Nk * kRowBytes, head_bytes);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(p.v + (size_t)bh * p.Nk * kRowBytes, head_bytes);
 
-  TileLoader<D, kWaves> ld;
+  TileLoader<D, DT, kWaves> ld;
   ld.init(wave, lane);
-  WaveState<D> st;
-  st.init(p.q + (size_t)bh * p.Nq * D, cx.qrow, p.Nq, lane);
+  WaveState<D, DT> st;
+  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane);
 
   // Scores (then probabilities) of even tiles live in (a0, a1), of odd
   // tiles in (b0, b1).
@@ -529,9 +715,9 @@ __global__ void __launch_bounds__(64 * kWaves) attn_fwd_kernel(Params p) {
 template <int D, int DT, bool CAUSAL>
 int launch_one(const Problem& pr, hipStream_t stream) {
   Params p;
-  p.q = (const uint16_t*)pr.q;
-  p.k = (const uint16_t*)pr.k;
-  p.v = (const uint16_t*)pr.v;
+  p.q = (const unsigned char*)pr.q;
+  p.k = (const unsigned char*)pr.k;
+  p.v = (const unsigned char*)pr.v;
   p.o = (uint16_t*)pr.o;
   p.lse = pr.lse;
   p.Nq = pr.Nq;
@@ -541,6 +727,7 @@ int launch_one(const Problem& pr, hipStream_t stream) {
   if (total > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   p.total_tiles = (int)total;
   p.c = pr.scale * kLog2e;
+  p.o_scale = pr.v_descale;
   hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL>), dim3(p.total_tiles), dim3(64 * kWaves), 0, stream, p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
@@ -553,6 +740,8 @@ int launch_head_dim(const Problem& p, hipStream_t s) {
       return p.causal ? launch_one<D, ATTN_F16, true>(p, s) : launch_one<D, ATTN_F16, false>(p, s);
     case ATTN_BF16:
       return p.causal ? launch_one<D, ATTN_BF16, true>(p, s) : launch_one<D, ATTN_BF16, false>(p, s);
+    case ATTN_FP8_E4M3:
+      return p.causal ? launch_one<D, ATTN_FP8_E4M3, true>(p, s) : launch_one<D, ATTN_FP8_E4M3, false>(p, s);
     default:
       return ATTN_ERR_DTYPE;
   }

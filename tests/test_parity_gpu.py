@@ -5,8 +5,12 @@ the same seeded inputs.  Tolerances are stated in tests/gpu_helpers.py.
   full-size ones (B=2,H=16,N=8192,d=128 and B=1,H=16,N=16384,d=256 causal)
   on sampled rows of sampled heads, in the launch configuration the
   benchmark times;
+* the E4M3 workload (B=2,H=16,N=8192,d=128 with 0.1% x20 outliers) on
+  sampled rows, gated on relative RMSE against the oracle run on the
+  dequantised inputs; the loss against the float32 values before
+  quantisation is printed, not gated;
 * edge shapes: N in {1, 17, 127, 129, 1000}, Nq != Nk both ways (including
-  causal rows with no visible key), every head dim, both 16-bit dtypes;
+  causal rows with no visible key), every head dim, every dtype;
 * invariants on the device: V = 1, Q = 0, bitwise determinism, a
   non-default stream, and canaries past the ends of o and lse.
 """
@@ -17,7 +21,11 @@ import torch
 
 import oracle
 from attention_forward_02_amd import attn_fwd, inputs, ATTN_F16, ATTN_BF16, ATTN_OK
-from gpu_helpers import compare, dequant, run_gpu, say, upload
+from gpu_helpers import compare, dequant, decode, fp8_lse_tol, out_dtype, run_gpu, say, upload
+
+
+def dequant_out(codes, dtype):
+    return decode(codes, out_dtype(dtype))
 
 pytestmark = pytest.mark.gpu
 
@@ -28,12 +36,13 @@ def _full_check(inp, label):
     o_codes, lse = run_gpu(inp)
     q, k, v = dequant(inp)
     o_ref, lse_ref = oracle.attention(q, k, v, inp.causal, float(inp.scale))
-    stats = compare(o_codes, lse, o_ref, lse_ref, inp.dtype, label)
+    ltol = fp8_lse_tol(q, k, float(inp.scale)) if inp.dtype == "e4m3" else None
+    stats = compare(o_codes, lse, o_ref, lse_ref, inp.dtype, label, lse_tol=ltol)
     say(f"[gpu] {label}: {stats}")
     return stats
 
 
-def _sampled_check(inp, label, heads, n_rows, seed):
+def _sampled_check(inp, label, heads, n_rows, seed, report_f32=False):
     say(f"[gpu] {label}: B={inp.B} H={inp.H} Nq={inp.Nq} Nk={inp.Nk} d={inp.d} "
         f"causal={inp.causal} dtype={inp.dtype} (sampled)")
     o_codes, lse = run_gpu(inp)
@@ -46,10 +55,16 @@ def _sampled_check(inp, label, heads, n_rows, seed):
     o_ref, lse_ref = oracle.attention(q, k, v, inp.causal, float(inp.scale), rows=rows)
     o_sel = np.stack([o_codes[b, h][rows] for b, h in heads])[None]
     l_sel = np.stack([lse[b, h][rows] for b, h in heads])[None]
-    stats = compare(o_sel, l_sel, o_ref, lse_ref, inp.dtype, label)
-    # every output of the whole tensor is finite and every LSE at least the row's own score bound
+    ltol = fp8_lse_tol(q, k, float(inp.scale))[:, :, rows] if inp.dtype == "e4m3" else None
+    stats = compare(o_sel, l_sel, o_ref, lse_ref, inp.dtype, label, lse_tol=ltol)
     assert np.isfinite(lse).all()
     say(f"[gpu] {label}: {stats} over {len(heads)} heads x {len(rows)} rows")
+    if report_f32:
+        sel = lambda x: np.stack([x[b, h] for b, h in heads])[None].astype(np.float64)
+        o32, _ = oracle.attention(sel(inp.q32), sel(inp.k32), sel(inp.v32), inp.causal, float(inp.scale), rows=rows)
+        o_gpu = dequant_out(o_sel, inp.dtype)
+        rel = float(np.linalg.norm(o_gpu - o32) / np.linalg.norm(o32))
+        say(f"[gpu] {label}: relative RMSE against the float32 inputs before quantisation {rel:.4g} (not gated)")
     return stats
 
 
@@ -71,17 +86,23 @@ def test_causal_d256_bf16_sampled():
     _sampled_check(inp, "causal_d256_bf16", heads=[(0, 0), (0, 7), (0, 15)], n_rows=40, seed=2)
 
 
+def test_hd128_seq8k_e4m3_sampled():
+    inp = inputs.make_workload("hd128_seq8k_e4m3", keep_f32=True)
+    _sampled_check(inp, "hd128_seq8k_e4m3", heads=[(0, 0), (0, 9), (1, 4), (1, 15)], n_rows=48, seed=3,
+                   report_f32=True)
+
+
 EDGE_N = [(1, 1), (17, 17), (127, 127), (129, 129), (1000, 1000), (1, 1000), (17, 129), (129, 17),
           (1000, 127), (300, 77)]
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "e4m3"])
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("nq,nk", EDGE_N, ids=[f"{a}x{b}" for a, b in EDGE_N])
 def test_edge_shapes(nq, nk, causal, d, dtype):
     seed = 7 + nq * 31 + nk * 17 + d + (1 if causal else 0)
-    inp = inputs.make(1, 2, nq, nk, d, dtype, seed=seed, causal=causal)
+    inp = inputs.make(1, 2, nq, nk, d, dtype, seed=seed, causal=causal, outliers=dtype == "e4m3")
     _full_check(inp, f"edge {nq}x{nk} d{d} {'causal' if causal else 'full'} {dtype}")
 
 

@@ -1,0 +1,219 @@
+"""rocprofv3 summaries of the attention kernel, and the HBM traffic figure
+the benchmark reports.
+
+    bash attention_forward_02_amd/profile_run.sh WORKLOAD OUTDIR    (on a GPU)
+    python -m attention_forward_02_amd.profiling OUTDIR WORKLOAD
+
+The first command runs, on one MI355X, a kernel trace of the benchmark
+command (`bench.py --no-cpu --workload WORKLOAD`), four counter passes of a
+short benchmark run, and the FETCH_SIZE / WRITE_SIZE passes of a plain
+1 GiB device copy.  The second turns the CSV output into
+`profiles/attn_fwd_kernel_<WORKLOAD>.md` and records the calibrated HBM
+bytes per launch in `profiles/traffic.json`, keyed by workload and stamped
+with the digest of the kernel sources, so `bench.py` reports them only
+while the kernel is the one that was profiled.
+
+Counter conventions on MI355X (8 XCDs, 256 CUs, 1024 SIMDs):
+* GRBM_GUI_ACTIVE is summed over the 8 XCDs: kernel cycles = value / 8.
+* SQ_VALU_MFMA_BUSY_CYCLES is summed over all SIMDs, so the MFMA-busy
+  fraction is value / (kernel cycles * 1024).
+* FETCH_SIZE and WRITE_SIZE are KiB per dispatch.  They are scaled by what
+  the same counter reads for the copy of a known byte count (the copy reads
+  and writes 1 GiB).
+"""
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_JSON = os.path.join(PROFILES, "traffic.json")
+
+KERNEL_SOURCES = ["csrc/attn_fwd_kernel.h", "csrc/attn_fwd_d64.hip", "csrc/attn_fwd_d128.hip",
+                  "csrc/attn_fwd_d256.hip", "csrc/attn_internal.h", "build.py"]
+KERNEL = "attn_fwd_kernel"
+N_XCD = 8
+N_SIMD = 1024
+COPY_BYTES = 1 << 30
+
+PMC_PASSES = [
+    ["FETCH_SIZE"],
+    ["WRITE_SIZE"],
+    ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"],
+    ["SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+]
+
+
+def kernel_digest():
+    """sha256 over the kernel's source files and build options."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """Calibrated HBM bytes per launch for `workload`, or None when no
+    profile exists or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_digest") != kernel_digest():
+        return None
+    return rec
+
+
+def _counters(path, name_filter):
+    """Per-dispatch mean of every counter for kernels whose name contains
+    `name_filter`."""
+    agg = defaultdict(float)
+    disp = set()
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if name_filter in r["Kernel_Name"]:
+                agg[r["Counter_Name"]] += float(r["Counter_Value"])
+                disp.add(r["Dispatch_Id"])
+    return {k: v / len(disp) for k, v in agg.items()}, len(disp)
+
+
+def _one(pattern):
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def summarize(outdir, workload):
+    from . import inputs
+    w = inputs.WORKLOADS[workload]
+    stats_rows = []
+    with open(_one(os.path.join(outdir, "trace", "**", "*kernel_stats.csv"))) as f:
+        for r in csv.DictReader(f):
+            stats_rows.append(r)
+    kern = [r for r in stats_rows if KERNEL in r["Name"]]
+    if len(kern) != 1:
+        raise RuntimeError(f"expected one {KERNEL} row in the kernel stats, found {len(kern)}")
+    k = kern[0]
+    avg_ns = float(k["AverageNs"])
+    c = {}
+    ndisp = {}
+    for i, names in enumerate(PMC_PASSES, 1):
+        v, n = _counters(_one(os.path.join(outdir, f"pmc{i}", "**", "*counter_collection.csv")), KERNEL)
+        c.update(v)
+        ndisp[i] = n
+    copy = {}
+    for name in ("FETCH_SIZE", "WRITE_SIZE"):
+        v, _ = _counters(_one(os.path.join(outdir, f"copy_{name}", "**", "*counter_collection.csv")), "copyBuffer")
+        copy[name] = v[name]
+    f_fetch = COPY_BYTES / (copy["FETCH_SIZE"] * 1024.0)
+    f_write = COPY_BYTES / (copy["WRITE_SIZE"] * 1024.0)
+    fetch_b = c["FETCH_SIZE"] * 1024.0 * f_fetch
+    write_b = c["WRITE_SIZE"] * 1024.0 * f_write
+    cycles = c["GRBM_GUI_ACTIVE"] / N_XCD
+    mfma_busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_SIMD)
+    lds_conf = c["SQ_LDS_BANK_CONFLICT"] / max(1.0, c["SQ_LDS_IDX_ACTIVE"])
+    fl = inputs.flops(w["B"], w["H"], w["Nq"], w["Nk"], w["d"], w["causal"])
+    elt = 1 if w["dtype"] == "e4m3" else 2
+    alg_read = 3 * w["B"] * w["H"] * w["Nq"] * w["d"] * elt if w["Nq"] == w["Nk"] else None
+    alg_write = w["B"] * w["H"] * w["Nq"] * (w["d"] * 2 + 4)
+    tflops = fl / (avg_ns * 1e-9) / 1e12
+    cmd_trace = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {outdir}/trace -o run -- "
+                 f"python3 bench.py --no-cpu --workload {workload}")
+    lines = [
+        f"# {KERNEL} on {workload}",
+        "",
+        f"Workload: B={w['B']} H={w['H']} Nq={w['Nq']} Nk={w['Nk']} d={w['d']} "
+        f"causal={w['causal']} dtype={w['dtype']}; one launch = {fl:.4g} FLOP.",
+        f"Kernel sources digest: `{kernel_digest()}`",
+        "",
+        "Made by (from the repository root, on one MI355X):",
+        "",
+        "```",
+        f"bash attention_forward_02_amd/profile_run.sh {workload} {outdir}",
+        f"python -m attention_forward_02_amd.profiling {outdir} {workload}",
+        "```",
+        "",
+        "## Kernel trace (`--kernel-trace --stats`)",
+        "",
+        "```",
+        cmd_trace,
+        "```",
+        "",
+        "| kernel | calls | average ns | min ns | max ns | TFLOP/s at average |",
+        "|---|---|---|---|---|---|",
+        f"| `{k['Name']}` | {k['Calls']} | {avg_ns:.0f} | {float(k['MinNs']):.0f} | {float(k['MaxNs']):.0f} "
+        f"| {tflops:.1f} |",
+        "",
+        "## Counters (`--pmc`, one pass each, per dispatch)",
+        "",
+        "```",
+    ]
+    for i, names in enumerate(PMC_PASSES, 1):
+        lines.append(f"timeout -s KILL 60 rocprofv3 --pmc {' '.join(names)} --output-format csv -d {outdir}/pmc{i} "
+                     f"-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu --workload {workload}")
+    for name in ("FETCH_SIZE", "WRITE_SIZE"):
+        lines.append(f"timeout -s KILL 60 rocprofv3 --pmc {name} --output-format csv -d {outdir}/copy_{name} "
+                     f"-o run -- python3 bench.py --copy-mib 1024 --steps 2 --warmup 1")
+    lines += [
+        "```",
+        "",
+        "| counter | value per dispatch |",
+        "|---|---|",
+    ]
+    for name in sorted(c):
+        lines.append(f"| {name} | {c[name]:.6g} |")
+    lines += [
+        "",
+        "| derived | value |",
+        "|---|---|",
+        f"| kernel cycles (GRBM_GUI_ACTIVE / 8 XCDs) | {cycles:.6g} |",
+        f"| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs)) | {100 * mfma_busy:.1f} % |",
+        f"| LDS bank conflict cycles / LDS active cycles | {lds_conf:.4f} |",
+        f"| VALU instructions per MFMA | {c['SQ_INSTS_VALU'] / max(1.0, c['SQ_INSTS_MFMA']):.2f} |",
+        f"| copy calibration FETCH_SIZE (1 GiB read) | {copy['FETCH_SIZE']:.6g} KiB -> factor {f_fetch:.4f} |",
+        f"| copy calibration WRITE_SIZE (1 GiB written) | {copy['WRITE_SIZE']:.6g} KiB -> factor {f_write:.4f} |",
+        f"| HBM read per launch (calibrated) | {fetch_b / 1e6:.1f} MB |",
+        f"| HBM write per launch (calibrated) | {write_b / 1e6:.1f} MB |",
+    ]
+    if alg_read is not None:
+        lines.append(f"| algorithmic read (Q, K, V once) / write (O, LSE) | {alg_read / 1e6:.1f} MB / "
+                     f"{alg_write / 1e6:.1f} MB |")
+    lines.append("")
+    os.makedirs(PROFILES, exist_ok=True)
+    md = os.path.join(PROFILES, f"{KERNEL}_{workload}.md")
+    with open(md, "w") as f:
+        f.write("\n".join(lines))
+    try:
+        with open(TRAFFIC_JSON) as f:
+            traffic = json.load(f)
+    except (OSError, ValueError):
+        traffic = {}
+    traffic[workload] = {
+        "bytes": round(fetch_b + write_b),
+        "fetch_bytes": round(fetch_b),
+        "write_bytes": round(write_b),
+        "fetch_factor": f_fetch,
+        "write_factor": f_write,
+        "kernel_digest": kernel_digest(),
+        "summary": os.path.relpath(md, ROOT),
+    }
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(traffic, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(f"wrote {md}; traffic {(fetch_b + write_b) / 1e6:.1f} MB per launch; "
+          f"kernel avg {avg_ns / 1e3:.1f} us; MFMA busy {100 * mfma_busy:.1f} %")
+
+
+if __name__ == "__main__":
+    if len(sys.argv) != 3:
+        sys.exit(__doc__)
+    summarize(sys.argv[1], sys.argv[2])

@@ -162,6 +162,11 @@ def main():
     fl = inputs.flops(inp.B, inp.H, inp.Nq, inp.Nk, inp.d, inp.causal)
     tflops = fl / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[inp.dtype]
+    # HBM bytes per launch from the committed rocprofv3 counter passes
+    # (FETCH_SIZE + WRITE_SIZE, copy-calibrated); None once the kernel
+    # sources differ from the ones profiled.
+    from attention_forward_02_amd.profiling import measured_traffic
+    tr = measured_traffic(args.workload)
     rec = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -178,7 +183,8 @@ def main():
         "config": {"workload": args.workload, "B": inp.B, "H": inp.H, "Nq": inp.Nq, "Nk": inp.Nk, "d": inp.d,
                    "causal": inp.causal, "in_dtype": inp.dtype, "flops_per_step": fl},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "frac": round(tflops / peak, 4), "traffic": tr["bytes"] if tr else None,
+                     "traffic_unit": "bytes per launch (HBM read + write)",
                      "kernel": "attn_fwd_kernel", "flops_per_launch": fl},
     }
     if not args.no_cpu:

@@ -492,25 +492,47 @@ struct LoopCtx {
   }
 };
 
-// Initial accumulators of tile t's scores, so that the score MFMAs apply the
-// mask themselves: 0 for visible keys, -inf for keys past Nk or above the
-// causal diagonal, and -inf everywhere for a tile the wave does not see (its
-// softmax then gives P = 0 and leaves m, l and O alone).  Returns false when
-// no element is masked (the MFMAs may then start from zero).
+// Whether tile t's scores need a mask bias: initial accumulators of 0 for
+// visible keys, -inf for keys past Nk or above the causal diagonal, and -inf
+// everywhere for a tile the wave does not see (its softmax then gives P = 0
+// and leaves m, l and O alone), so that the score MFMAs apply the mask
+// themselves.  Wave-uniform; false for all but the last tile of a
+// non-causal row and the diagonal tiles of a causal one.
 template <bool CAUSAL>
-__device__ __forceinline__ bool score_bias(const LoopCtx& cx, int t, f32x16& s0, f32x16& s1) {
-  const bool vis = cx.visible(t);
-  if (vis && !cx.needs_mask<CAUSAL>(t)) return false;
-  mask_bias(s0, s1, vis ? cx.mask_rem<CAUSAL>(t) : -(1 << 30));
-  return true;
+__device__ __forceinline__ bool needs_bias(const LoopCtx& cx, int t) {
+  return !cx.visible(t) || cx.needs_mask<CAUSAL>(t);
 }
 
-// Scores of tile t (K from Ks) into (s0, s1), masked through the bias.
-template <int D, int DT, bool CAUSAL>
+// The first tile for which needs_bias holds (every later tile needs one
+// too): min(nt, the ragged last tile Nk / 64, and for causal the first tile
+// whose last key lies past the wave's first row's diagonal).  A tile the
+// wave cannot see lies past that diagonal as well.
+template <bool CAUSAL>
+__device__ __forceinline__ int first_bias_tile(const LoopCtx& cx) {
+  int t = min(cx.nt, cx.Nk / kBlockN);
+  if (CAUSAL) {
+    const int x = cx.qw0 + cx.diag - (kBlockN - 2);  // tile t is crossed iff 64 t >= x
+    t = min(t, x <= 0 ? 0 : (x + kBlockN - 1) / kBlockN);
+  }
+  return t;
+}
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
+// Scores of tile t (K from Ks) into (s0, s1).  MASKED: the accumulators
+// start from the tile's mask bias (see score_bias); else from zero.
+template <int D, int DT, bool CAUSAL, bool MASKED>
 __device__ __forceinline__ void masked_scores(const WaveState<D, DT>& st, const LoopCtx& cx, int t,
                                               const lds_t* Ks, f32x16& s0, f32x16& s1) {
-  if (score_bias<CAUSAL>(cx, t, s0, s1)) tile_scores<D, DT, true>(st, Ks, s0, s1);
-  else tile_scores<D, DT, false>(st, Ks, s0, s1);
+  if constexpr (MASKED) {
+    mask_bias(s0, s1, cx.visible(t) ? cx.mask_rem<CAUSAL>(t) : -(1 << 30));
+    tile_scores<D, DT, true>(st, Ks, s0, s1);
+  } else {
+    tile_scores<D, DT, false>(st, Ks, s0, s1);
+  }
 }
 
 // Reference update from a tile's row max (in units of scale*log2(e)):
@@ -525,13 +547,14 @@ __device__ __forceinline__ float update_reference(float& m2, float m2t, bool& re
 }
 
 // Instruction interleave of one phase: after `pre` LDS reads, `n` groups of
-// one MFMA, `valu` VALU instructions and `reads` LDS reads.
+// one MFMA, `valu` VALU or transcendental instructions (mask 0x402: v_exp_f32
+// is not in the plain VALU class) and `reads` LDS reads.
 #define ATTN_INTERLEAVE(pre, n, valu, reads)                  \
   do {                                                        \
     __builtin_amdgcn_sched_group_barrier(0x100, pre, 0);      \
     _Pragma("unroll") for (int i_ = 0; i_ < (n); ++i_) {      \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      \
-      __builtin_amdgcn_sched_group_barrier(0x002, valu, 0);   \
+      __builtin_amdgcn_sched_group_barrier(0x402, valu, 0);   \
       __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);  \
     }                                                         \
     __builtin_amdgcn_sched_barrier(0);                        \
@@ -545,12 +568,14 @@ __device__ __forceinline__ float update_reference(float& m2, float m2t, bool& re
 //                                                         row max of S_{j+1},
 //                                                         reference update
 // then, rarely, O and l are rescaled to the new reference.  s0, s1 hold S_j
-// on entry (and p_j after phase A).
-template <int D, int DT, bool CAUSAL>
+// on entry (and p_j after phase A).  The mask choice is a template
+// parameter, taken by a wave-uniform branch around the whole step, so each
+// phase is one basic block and its interleave holds.
+template <int D, int DT, bool CAUSAL, bool MASKED>
 __device__ __forceinline__ void step(WaveState<D, DT>& st, const LoopCtx& cx, int j, f32x16& s0, f32x16& s1,
                                      f32x16& n0, f32x16& n1, const lds_t* Kn, const lds_t* Vs) {
   // Phase A
-  masked_scores<D, DT, CAUSAL>(st, cx, j + 1, Kn, n0, n1);
+  masked_scores<D, DT, CAUSAL, MASKED>(st, cx, j + 1, Kn, n0, n1);
   const float mref = (st.m2 == -__builtin_inff()) ? 0.f : st.m2;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -571,7 +596,10 @@ __device__ __forceinline__ void step(WaveState<D, DT>& st, const LoopCtx& cx, in
     pf[1] = pack8<DT>(s0, 8);
     pf[2] = pack8<DT>(s1, 0);
     pf[3] = pack8<DT>(s1, 8);
-    ATTN_INTERLEAVE(3, D / 8, 5, 1);
+    // D/8 MFMAs of 32 cycles per phase, one K read each; the 80 VALU
+    // instructions of phase A (32 FMA, 32 exp2, 16 packs) spread evenly.
+    constexpr int kValuA = (80 + D / 8 - 1) / (D / 8);
+    ATTN_INTERLEAVE(3, D / 8, kValuA, 1);
     // Phase B
     pv_tile<D, DT>(st, pf, Vs);
   }
@@ -590,9 +618,16 @@ __device__ __forceinline__ void step(WaveState<D, DT>& st, const LoopCtx& cx, in
     else if constexpr (D == 128) ATTN_INTERLEAVE(4, 4, 15, 4);
     else ATTN_INTERLEAVE(4, 8, 8, 4);
   } else {
-    ATTN_INTERLEAVE(4, D / 8, 4, 2);
+    // About 64 VALU instructions (32 adds, 16 max3, the reference update).
+    constexpr int kValuB = (64 + D / 8 - 1) / (D / 8);
+    ATTN_INTERLEAVE(4, D / 8, kValuB, 2);
   }
   if (rescale) {
+    // The empty asm keeps this block a real (wave-uniform, rarely taken)
+    // branch: without it the compiler speculates the multiplies, since on
+    // 16-wide vectors they look cheap, and would scale O by alpha = 1 on
+    // every tile.
+    asm volatile("" ::: "memory");
     st.lrun *= alpha;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha;
@@ -678,6 +713,13 @@ __global__ void __launch_bounds__(64 * kWaves) attn_fwd_kernel(Params p) {
   // Scores (then probabilities) of even tiles live in (a0, a1), of odd
   // tiles in (b0, b1).
   f32x16 a0, a1, b0, b1;
+  // Tiles before tb need no mask bias; step j works on the scores of tile
+  // j + 1, so steps j < jm (jm even, so the second loop again starts with
+  // S_j in (a0, a1)) run the unmasked step and the rest the masked one.  Two
+  // loops with one step variant each keep the register assignment of the
+  // unrolled pair identical on every iteration.
+  const int tb = first_bias_tile<CAUSAL>(cx);
+  const int jm = tb > 1 ? (tb - 1) & ~1 : 0;
   if (nt > 0) {
     // K_1 is loaded even when there is no tile 1: its rows then fail the
     // range check and arrive as zeros, so every K stage a step reads holds
@@ -687,25 +729,33 @@ __global__ void __launch_bounds__(64 * kWaves) attn_fwd_kernel(Params p) {
     ld.load(K1, Kr, kBlockN);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    masked_scores<D, DT, CAUSAL>(st, cx, 0, K0, a0, a1);
+    if (tb > 0) masked_scores<D, DT, CAUSAL, false>(st, cx, 0, K0, a0, a1);
+    else masked_scores<D, DT, CAUSAL, true>(st, cx, 0, K0, a0, a1);
     bool rescale;
     update_reference(st.m2, tile_max2(a0, a1, cx.c), rescale);
   }
-  for (int j = 0; j < nt; j += 2) {
+  // One even and one odd step; returns false after the last step.
+  auto two_steps = [&](int j, auto masked) -> bool {
+    constexpr bool M = decltype(masked)::value;
     // Even step: (a0, a1) = S_j; K_{j+1} in K1, V_j in V0; K_{j+2} -> K0, V_{j+1} -> V1.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (j + 2 < nt) ld.load(K0, Kr, (j + 2) * kBlockN);
     if (j + 1 < nt) ld.load(V1, Vr, (j + 1) * kBlockN);
-    step<D, DT, CAUSAL>(st, cx, j, a0, a1, b0, b1, K1, V0);
-    if (j + 1 >= nt) break;
+    step<D, DT, CAUSAL, M>(st, cx, j, a0, a1, b0, b1, K1, V0);
+    if (j + 1 >= nt) return false;
     // Odd step: (b0, b1) = S_{j+1}; K_{j+2} in K0, V_{j+1} in V1; K_{j+3} -> K1, V_{j+2} -> V0.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (j + 3 < nt) ld.load(K1, Kr, (j + 3) * kBlockN);
     if (j + 2 < nt) ld.load(V0, Vr, (j + 2) * kBlockN);
-    step<D, DT, CAUSAL>(st, cx, j + 1, b0, b1, a0, a1, K0, V1);
-  }
+    step<D, DT, CAUSAL, M>(st, cx, j + 1, b0, b1, a0, a1, K0, V1);
+    return true;
+  };
+  int j = 0;
+  for (; j < jm; j += 2) two_steps(j, BoolTag<false>{});
+  for (; j < nt; j += 2)
+    if (!two_steps(j, BoolTag<true>{})) break;
   store_output<D, DT>(p, st, bh, cx.qrow, cx.half);
 }
 

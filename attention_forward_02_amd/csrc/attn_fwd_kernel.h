@@ -390,14 +390,16 @@ __device__ __forceinline__ void tile_scores(const WaveState8<D>& st, const lds_t
   }
 }
 
-// O^T += V^T P^T for one tile, V from LDS through transpose reads.
+// O^T += V^T P^T for one tile, V from LDS through transpose reads.  The
+// k-step loop is outermost so that consecutive MFMAs accumulate into
+// different 32-column blocks of O.
 template <int D, int DT>
 __device__ __forceinline__ void pv_tile(WaveState16<D, DT>& st, const i16x8 (&pf)[4], const lds_t* Vs) {
   constexpr int kRowBytes = D * 2;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+  for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int db = 0; db < D / 32; ++db) {
       const lds_t* base = Vs + (db >> 2) * 256 + 16 * ks * kRowBytes;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + st.voff[db & 3][0]));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + st.voff[db & 3][1]));
@@ -602,14 +604,38 @@ __device__ __forceinline__ void step(WaveState<D, DT>& st, const LoopCtx& cx, in
     ATTN_INTERLEAVE(3, D / 8, kValuA, 1);
     // Phase B
     pv_tile<D, DT>(st, pf, Vs);
-  }
-  float ls0 = 0.f, ls1 = 0.f;
+    if constexpr (DT == ATTN_F16) {
+      // Row sum from the packed binary16 P with v_dot2_f32_f16 against
+      // (1, 1): half the instructions of fp32 adds.  It sums P as rounded
+      // for the MFMA (relative error below 2^-11 per term, so |dLSE| stays
+      // below 5e-4 in the worst case), which also makes the normalisation
+      // consistent with the P V product.  bfloat16's coarser rounding could
+      // move LSE by up to 2e-3, so bf16 keeps the fp32 sum of unrounded p.
+      float l[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    ls0 += s0[r];
-    ls1 += s1[r];
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 w = __builtin_bit_cast(u32x4, pf[i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // Copy the element out first: a bit cast applied directly to a
+          // vector element reads element 0.
+          const uint32_t we = w[e];
+          l[e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, we), (f16x2){(_Float16)1.0f, (_Float16)1.0f}, l[e],
+                                        false);
+        }
+      }
+      st.lrun += (l[0] + l[1]) + (l[2] + l[3]);
+    }
   }
-  st.lrun += ls0 + ls1;
+  if constexpr (DT != ATTN_F16) {
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      ls0 += s0[r];
+      ls1 += s1[r];
+    }
+    st.lrun += ls0 + ls1;
+  }
   bool rescale;
   const float alpha = update_reference(st.m2, tile_max2(n0, n1, cx.c), rescale);
   if constexpr (DT == ATTN_FP8_E4M3) {
@@ -619,7 +645,7 @@ __device__ __forceinline__ void step(WaveState<D, DT>& st, const LoopCtx& cx, in
     else ATTN_INTERLEAVE(4, 8, 8, 4);
   } else {
     // About 64 VALU instructions (32 adds, 16 max3, the reference update).
-    constexpr int kValuB = (64 + D / 8 - 1) / (D / 8);
+    constexpr int kValuB = ((DT == ATTN_F16 ? 48 : 64) + D / 8 - 1) / (D / 8);
     ATTN_INTERLEAVE(4, D / 8, kValuB, 2);
   }
   if (rescale) {

@@ -43,6 +43,9 @@ SOURCES = [
     ("attn_fwd_d64.hip", VGPR_FORM),
     ("attn_fwd_d128.hip", VGPR_FORM),
     ("attn_fwd_d256.hip", VGPR_FORM),
+    ("attn_fwd_d64_fp8.hip", VGPR_FORM),
+    ("attn_fwd_d128_fp8.hip", VGPR_FORM),
+    ("attn_fwd_d256_fp8.hip", VGPR_FORM),
 ]
 
 

@@ -1,0 +1,16 @@
+// Attention forward kernels for head dimension 128, E4M3 inputs (device code in
+// attn_fwd_kernel.h).  Explicit instantiations make the host pass emit a
+// launch stub for every kernel the dispatcher can launch.
+#include "attn_fwd_kernel.h"
+
+namespace attn {
+namespace kernels {
+
+template __global__ void attn_fwd_kernel<128, ATTN_FP8_E4M3, false>(Params);
+template __global__ void attn_fwd_kernel<128, ATTN_FP8_E4M3, true>(Params);
+
+}  // namespace kernels
+
+int launch_forward_d128_fp8(const Problem& p, hipStream_t stream) { return kernels::launch_fp8<128>(p, stream); }
+
+}  // namespace attn

@@ -550,7 +550,9 @@ __device__ __forceinline__ float update_reference(float& m2, float m2t, bool& re
 
 // Instruction interleave of one phase: after `pre` LDS reads, `n` groups of
 // one MFMA, `valu` VALU or transcendental instructions (mask 0x402: v_exp_f32
-// is not in the plain VALU class) and `reads` LDS reads.
+// is not in the plain VALU class) and `reads` LDS reads.  Both phases of a
+// step form one scheduling region, so the first V reads of phase B may be
+// issued under the last MFMAs of phase A.
 #define ATTN_INTERLEAVE(pre, n, valu, reads)                  \
   do {                                                        \
     __builtin_amdgcn_sched_group_barrier(0x100, pre, 0);      \
@@ -559,7 +561,6 @@ __device__ __forceinline__ float update_reference(float& m2, float m2t, bool& re
       __builtin_amdgcn_sched_group_barrier(0x402, valu, 0);   \
       __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);  \
     }                                                         \
-    __builtin_amdgcn_sched_barrier(0);                        \
   } while (0)
 
 // One step of the key loop for tile j, as two MFMA blocks with the softmax
@@ -576,7 +577,9 @@ __device__ __forceinline__ float update_reference(float& m2, float m2t, bool& re
 template <int D, int DT, bool CAUSAL, bool MASKED>
 __device__ __forceinline__ void step(WaveState<D, DT>& st, const LoopCtx& cx, int j, f32x16& s0, f32x16& s1,
                                      f32x16& n0, f32x16& n1, const lds_t* Kn, const lds_t* Vs) {
-  // Phase A
+  // Phase A.  At d = 256 (one wave per SIMD, so the SIMD's other waves are
+  // the workgroup's own) the wave in its exp-heavy phase gets issue priority.
+  if constexpr (D >= 256) __builtin_amdgcn_s_setprio(1);
   masked_scores<D, DT, CAUSAL, MASKED>(st, cx, j + 1, Kn, n0, n1);
   const float mref = (st.m2 == -__builtin_inff()) ? 0.f : st.m2;
 #pragma unroll
@@ -627,6 +630,7 @@ __device__ __forceinline__ void step(WaveState<D, DT>& st, const LoopCtx& cx, in
       st.lrun += (l[0] + l[1]) + (l[2] + l[3]);
     }
   }
+  if constexpr (D >= 256) __builtin_amdgcn_s_setprio(0);
   if constexpr (DT != ATTN_F16) {
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
@@ -648,6 +652,7 @@ __device__ __forceinline__ void step(WaveState<D, DT>& st, const LoopCtx& cx, in
     constexpr int kValuB = ((DT == ATTN_F16 ? 48 : 64) + D / 8 - 1) / (D / 8);
     ATTN_INTERLEAVE(4, D / 8, kValuB, 2);
   }
+  __builtin_amdgcn_sched_barrier(0);
   if (rescale) {
     // The empty asm keeps this block a real (wave-uniform, rarely taken)
     // branch: without it the compiler speculates the multiplies, since on
@@ -808,19 +813,24 @@ int launch_one(const Problem& pr, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-// Dispatch one head dimension over dtype and causality.
+// Dispatch one head dimension over the 16-bit dtypes and causality.
 template <int D>
-int launch_head_dim(const Problem& p, hipStream_t s) {
+int launch_16bit(const Problem& p, hipStream_t s) {
   switch (p.dtype) {
     case ATTN_F16:
       return p.causal ? launch_one<D, ATTN_F16, true>(p, s) : launch_one<D, ATTN_F16, false>(p, s);
     case ATTN_BF16:
       return p.causal ? launch_one<D, ATTN_BF16, true>(p, s) : launch_one<D, ATTN_BF16, false>(p, s);
-    case ATTN_FP8_E4M3:
-      return p.causal ? launch_one<D, ATTN_FP8_E4M3, true>(p, s) : launch_one<D, ATTN_FP8_E4M3, false>(p, s);
     default:
       return ATTN_ERR_DTYPE;
   }
+}
+
+// E4M3, one head dimension.
+template <int D>
+int launch_fp8(const Problem& p, hipStream_t s) {
+  if (p.dtype != ATTN_FP8_E4M3) return ATTN_ERR_DTYPE;
+  return p.causal ? launch_one<D, ATTN_FP8_E4M3, true>(p, s) : launch_one<D, ATTN_FP8_E4M3, false>(p, s);
 }
 
 }  // namespace kernels

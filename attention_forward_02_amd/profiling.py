@@ -36,7 +36,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_JSON = os.path.join(PROFILES, "traffic.json")
 
 KERNEL_SOURCES = ["csrc/attn_fwd_kernel.h", "csrc/attn_fwd_d64.hip", "csrc/attn_fwd_d128.hip",
-                  "csrc/attn_fwd_d256.hip", "csrc/attn_internal.h", "build.py"]
+                  "csrc/attn_fwd_d256.hip", "csrc/attn_fwd_d64_fp8.hip", "csrc/attn_fwd_d128_fp8.hip",
+                  "csrc/attn_fwd_d256_fp8.hip", "csrc/attn_internal.h", "build.py"]
 KERNEL = "attn_fwd_kernel"
 N_XCD = 8
 N_SIMD = 1024

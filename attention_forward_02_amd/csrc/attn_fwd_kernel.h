@@ -28,8 +28,8 @@
 //   * exp is v_exp_f32 (2^x) on scores pre-multiplied by scale * log2(e);
 //     LSE is converted back to natural log at the end.
 //
-// Schedule (4 waves, 128 query rows per workgroup, two workgroups per CU at
-// d <= 128 so that every SIMD runs two waves): each step overlaps the score
+// Schedule (32 query rows per wave; at d <= 128 every SIMD runs two waves,
+// see Waves below): each step overlaps the score
 // MFMAs of the next tile with the exponentials of the current one, and the
 // P V MFMAs with the row sums and the next tile's row max (the pages'
 // two-stage overlap of matrix multiplies and softmax), so the matrix core
@@ -691,11 +691,21 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<D,
   }
 }
 
-constexpr int kWaves = 4;
-constexpr int kBlockM = kWaves * kRowsPerWave;  // query rows per workgroup
+// Waves per workgroup (32 query rows each).  At d = 128 with 16-bit inputs
+// one 8-wave workgroup per CU (two waves per SIMD, 256 query rows) shares
+// each K/V tile among twice the rows of two 4-wave workgroups, halving the
+// global-to-LDS loads per FLOP; measured faster there.  Elsewhere 4 waves:
+// E4M3 at d = 128 and d = 64 measured slower with 8, and d = 256 needs one
+// workgroup's whole LDS share for its 4 waves.
+template <int D, int DT>
+struct Waves {
+  static constexpr int value = (D == 128 && DT != ATTN_FP8_E4M3) ? 8 : 4;
+};
 
 template <int D, int DT, bool CAUSAL>
-__global__ void __launch_bounds__(64 * kWaves) attn_fwd_kernel(Params p) {
+__global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_kernel(Params p) {
+  constexpr int kWaves = Waves<D, DT>::value;
+  constexpr int kBlockM = kWaves * kRowsPerWave;  // query rows per workgroup
   constexpr int kRowBytes = D * Fmt<DT>::kBytes;
   constexpr int kTileBytes = kBlockN * kRowBytes;
   // K and V rings of two stages each, as four separate LDS objects.  K runs
@@ -803,6 +813,8 @@ int launch_one(const Problem& pr, hipStream_t stream) {
   p.lse = pr.lse;
   p.Nq = pr.Nq;
   p.Nk = pr.Nk;
+  constexpr int kWaves = Waves<D, DT>::value;
+  constexpr int kBlockM = kWaves * kRowsPerWave;
   p.n_qtiles = (pr.Nq + kBlockM - 1) / kBlockM;
   const long long total = (long long)pr.B * pr.H * p.n_qtiles;
   if (total > 0x7fffffffLL) return ATTN_ERR_SHAPE;

@@ -691,15 +691,15 @@ __device__ __forceinline__ void store_output(const Params& p, const WaveState<D,
   }
 }
 
-// Waves per workgroup (32 query rows each).  At d = 128 with 16-bit inputs
-// one 8-wave workgroup per CU (two waves per SIMD, 256 query rows) shares
-// each K/V tile among twice the rows of two 4-wave workgroups, halving the
+// Waves per workgroup (32 query rows each).  At d = 128 one 8-wave
+// workgroup per CU (two waves per SIMD, 256 query rows) shares each K/V
+// tile among twice the rows of two 4-wave workgroups, halving the
 // global-to-LDS loads per FLOP; measured faster there.  Elsewhere 4 waves:
-// E4M3 at d = 128 and d = 64 measured slower with 8, and d = 256 needs one
-// workgroup's whole LDS share for its 4 waves.
+// d = 64 measured slower with 8, and d = 256 needs one workgroup's whole LDS
+// share for its 4 waves.
 template <int D, int DT>
 struct Waves {
-  static constexpr int value = (D == 128 && DT != ATTN_FP8_E4M3) ? 8 : 4;
+  static constexpr int value = D == 128 ? 8 : 4;
 };
 
 template <int D, int DT, bool CAUSAL>
@@ -801,6 +801,136 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_kernel(Pa
 }
 
 // ---------------------------------------------------------------------------
+// Sequential-step kernel: the same tile loop without software pipelining of
+// the scores.  Each step computes S_j, its softmax and O += P_j V_j in
+// order; the overlap of matrix work and softmax comes from the other waves
+// of the SIMD instead of from within the wave.  Used where the softmax VALU
+// work, not the matrix core, bounds the step (E4M3 at d = 128, where one
+// 64-cycle MFMA carries the softmax of 32 scores per lane): without the
+// second score tile in registers the step is simpler and measured faster.
+// K_j and V_j share a ring stage; the loads of tile j + 1 are issued at the
+// start of step j.
+// ---------------------------------------------------------------------------
+template <int D, int DT, bool CAUSAL, bool MASKED>
+__device__ __forceinline__ void seq_step(WaveState<D, DT>& st, const LoopCtx& cx, int j, const lds_t* Kc,
+                                         const lds_t* Vc) {
+  f32x16 s0, s1;
+  masked_scores<D, DT, CAUSAL, MASKED>(st, cx, j, Kc, s0, s1);
+  bool rescale;
+  const float alpha = update_reference(st.m2, tile_max2(s0, s1, cx.c), rescale);
+  if (rescale) {
+    asm volatile("" ::: "memory");  // keep the branch (see step)
+    st.lrun *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha;
+  }
+  const float mref = (st.m2 == -__builtin_inff()) ? 0.f : st.m2;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cx.c, -mref));
+    s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cx.c, -mref));
+  }
+  if constexpr (DT == ATTN_FP8_E4M3) {
+    pv_tile<D>(st, pack_p_fp8(s0, s1), Vc);
+  } else {
+    i16x8 pf[4];
+    pf[0] = pack8<DT>(s0, 0);
+    pf[1] = pack8<DT>(s0, 8);
+    pf[2] = pack8<DT>(s1, 0);
+    pf[3] = pack8<DT>(s1, 8);
+    pv_tile<D, DT>(st, pf, Vc);
+  }
+  float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    ls0 += s0[r];
+    ls1 += s1[r];
+  }
+  st.lrun += ls0 + ls1;
+}
+
+template <int D, int DT, bool CAUSAL>
+__global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_seq_kernel(Params p) {
+  constexpr int kWaves = Waves<D, DT>::value;
+  constexpr int kBlockM = kWaves * kRowsPerWave;
+  constexpr int kRowBytes = D * Fmt<DT>::kBytes;
+  constexpr int kTileBytes = kBlockN * kRowBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st1[kTileBytes];
+  lds_t* const K0 = (lds_t*)k_st0;
+  lds_t* const K1 = (lds_t*)k_st1;
+  lds_t* const V0 = (lds_t*)v_st0;
+  lds_t* const V1 = (lds_t*)v_st1;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int bh, qt;
+  schedule(p, blockIdx.x, CAUSAL, bh, qt);
+  const int q0 = qt * kBlockM;
+  LoopCtx cx;
+  cx.qw0 = q0 + wave * kRowsPerWave;
+  cx.qrow = cx.qw0 + (lane & 31);
+  cx.diag = p.Nk - p.Nq;
+  cx.Nk = p.Nk;
+  cx.half = lane >> 5;
+  cx.c = p.c;
+  cx.wave_kend = CAUSAL ? cx.qw0 + kRowsPerWave - 1 + cx.diag : p.Nk;
+  int kend = p.Nk;
+  if (CAUSAL) kend = min(p.Nk, q0 + kBlockM + cx.diag);
+  const int nt = kend > 0 ? (kend + kBlockN - 1) / kBlockN : 0;
+  cx.nt = nt;
+
+  const uint32_t head_bytes = (uint32_t)p.Nk * kRowBytes;
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(p.k + (size_t)bh * p.Nk * kRowBytes, head_bytes);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(p.v + (size_t)bh * p.Nk * kRowBytes, head_bytes);
+  TileLoader<D, DT, kWaves> ld;
+  ld.init(wave, lane);
+  WaveState<D, DT> st;
+  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane);
+
+  if (nt > 0) {
+    ld.load(K0, Kr, 0);
+    ld.load(V0, Vr, 0);
+  }
+  // Tiles before tb need no mask bias: steps j < jm (jm even) run the
+  // unmasked step, the rest the masked one (two loops, one step variant
+  // each).
+  const int tb = min(first_bias_tile<CAUSAL>(cx), nt);
+  const int jm = tb & ~1;
+  // Step j: K_j, V_j in (Kc, Vc); tile j + 1 -> (Kl, Vl).
+  auto step = [&](int j, const lds_t* Kc, const lds_t* Vc, lds_t* Kl, lds_t* Vl, auto masked) {
+    constexpr bool M = decltype(masked)::value;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 1 < nt) {
+      ld.load(Kl, Kr, (j + 1) * kBlockN);
+      ld.load(Vl, Vr, (j + 1) * kBlockN);
+    }
+    seq_step<D, DT, CAUSAL, M>(st, cx, j, Kc, Vc);
+  };
+  int j = 0;
+  for (; j < jm; j += 2) {
+    step(j, K0, V0, K1, V1, BoolTag<false>{});
+    step(j + 1, K1, V1, K0, V0, BoolTag<false>{});
+  }
+  for (; j < nt; j += 2) {
+    step(j, K0, V0, K1, V1, BoolTag<true>{});
+    if (j + 1 >= nt) break;
+    step(j + 1, K1, V1, K0, V0, BoolTag<true>{});
+  }
+  store_output<D, DT>(p, st, bh, cx.qrow, cx.half);
+}
+
+// Which loop a (head dim, format) uses: the sequential-step kernel for
+// E4M3 at d = 128, the pipelined one elsewhere.
+template <int D, int DT>
+struct Sequential {
+  static constexpr bool value = (D == 128 && DT == ATTN_FP8_E4M3);
+};
+
+// ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
 template <int D, int DT, bool CAUSAL>
@@ -821,7 +951,10 @@ int launch_one(const Problem& pr, hipStream_t stream) {
   p.total_tiles = (int)total;
   p.c = pr.scale * kLog2e;
   p.o_scale = pr.v_descale;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL>), dim3(p.total_tiles), dim3(64 * kWaves), 0, stream, p);
+  if constexpr (Sequential<D, DT>::value)
+    hipLaunchKernelGGL((attn_fwd_seq_kernel<D, DT, CAUSAL>), dim3(p.total_tiles), dim3(64 * kWaves), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL>), dim3(p.total_tiles), dim3(64 * kWaves), 0, stream, p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

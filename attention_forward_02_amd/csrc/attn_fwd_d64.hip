@@ -11,6 +11,10 @@ template __global__ void attn_fwd_kernel<64, ATTN_F16, true>(Params);
 template __global__ void attn_fwd_kernel<64, ATTN_BF16, false>(Params);
 template __global__ void attn_fwd_kernel<64, ATTN_BF16, true>(Params);
 
+template __global__ void attn_fwd_split_kernel<64, ATTN_F16, false>(Params);
+template __global__ void attn_fwd_split_kernel<64, ATTN_F16, true>(Params);
+template __global__ void attn_fwd_split_kernel<64, ATTN_BF16, false>(Params);
+template __global__ void attn_fwd_split_kernel<64, ATTN_BF16, true>(Params);
 }  // namespace kernels
 
 int launch_forward_d64(const Problem& p, hipStream_t stream) { return kernels::launch_16bit<64>(p, stream); }

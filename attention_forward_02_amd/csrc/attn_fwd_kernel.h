@@ -923,6 +923,148 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_seq_kerne
   store_output<D, DT>(p, st, bh, cx.qrow, cx.half);
 }
 
+// ---------------------------------------------------------------------------
+// Split-key kernel for small grids (16-bit, d = 64): each 128-row query tile
+// gets an 8-wave workgroup whose two 4-wave groups walk the two halves of the
+// tile's key range at the same time, each through its own K/V ring, and
+// merge at the end -- group B hands (m, l, O) to group A through LDS, which
+// rescales both partial results to the larger maximum and adds them (the
+// online-softmax rescale of the concept card's sketch, applied once across
+// the split).  Halves the sequential key loop of the longest query tiles,
+// which is the critical path when there are about as many query tiles as
+// CUs.
+// ---------------------------------------------------------------------------
+template <int D, int DT, bool CAUSAL>
+__global__ void __launch_bounds__(512) attn_fwd_split_kernel(Params p) {
+  static_assert(D == 64 && DT != ATTN_FP8_E4M3, "split-key kernel: 16-bit, d = 64");
+  constexpr int kGroupWaves = 4;
+  constexpr int kBlockM = kGroupWaves * kRowsPerWave;  // 128 query rows
+  constexpr int kRowBytes = D * 2;
+  constexpr int kTileBytes = kBlockN * kRowBytes;
+  constexpr int kAcc = D / 32 * 16;  // O accumulator floats per lane
+  // Two rings (group A, group B), each with two K and two V stages.
+  __shared__ __attribute__((aligned(1024))) unsigned char ka0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char ka1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char va0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char va1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char kb0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char kb1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb1[kTileBytes];
+  // Group B's partial results, [row block][m, l, O...][lane].
+  __shared__ float xch[kGroupWaves][kAcc + 2][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rb = wave & 3, grp = wave >> 2;
+
+  int bh, qt;
+  schedule(p, blockIdx.x, CAUSAL, bh, qt);
+  const int q0 = qt * kBlockM;
+  int kend = p.Nk;
+  if (CAUSAL) kend = min(p.Nk, q0 + kBlockM + (p.Nk - p.Nq));
+  const int nt = kend > 0 ? (kend + kBlockN - 1) / kBlockN : 0;
+  const int mid = (nt + 1) / 2;                 // group A: tiles [0, mid)
+  const int j0 = grp ? mid : 0, j1 = grp ? nt : mid;  // this group's tiles
+  LoopCtx cx;
+  cx.qw0 = q0 + rb * kRowsPerWave;
+  cx.qrow = cx.qw0 + (lane & 31);
+  cx.diag = p.Nk - p.Nq;
+  cx.Nk = p.Nk;
+  cx.half = lane >> 5;
+  cx.c = p.c;
+  cx.wave_kend = CAUSAL ? cx.qw0 + kRowsPerWave - 1 + cx.diag : p.Nk;
+  cx.nt = j1;  // tiles from j1 on belong to the other group (or do not exist)
+
+  const uint32_t head_bytes = (uint32_t)p.Nk * kRowBytes;
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(p.k + (size_t)bh * p.Nk * kRowBytes, head_bytes);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(p.v + (size_t)bh * p.Nk * kRowBytes, head_bytes);
+  TileLoader<D, DT, kGroupWaves> ld;
+  ld.init(rb, lane);
+  WaveState<D, DT> st;
+  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane);
+
+  // The key loop of one group over tiles [j0, j1), as in attn_fwd_kernel.
+  // Every group executes the same number of barriers: 1 + (mid + 1) / 2
+  // loop pairs, steps past its range being barrier-only.
+  const int pairs = (mid + 1) / 2;
+  auto run = [&](lds_t* K0, lds_t* K1, lds_t* V0, lds_t* V1) {
+    f32x16 a0, a1, b0, b1;
+    const int len = j1 - j0;
+    if (len > 0) {
+      ld.load(K0, Kr, j0 * kBlockN);
+      ld.load(V0, Vr, j0 * kBlockN);
+      ld.load(K1, Kr, (j0 + 1) * kBlockN);  // zeros or finite data when past the range
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int tb = first_bias_tile<CAUSAL>(cx);
+    if (len > 0) {
+      if (tb > j0) masked_scores<D, DT, CAUSAL, false>(st, cx, j0, K0, a0, a1);
+      else masked_scores<D, DT, CAUSAL, true>(st, cx, j0, K0, a0, a1);
+      bool rescale;
+      update_reference(st.m2, tile_max2(a0, a1, cx.c), rescale);
+    }
+    auto two_steps = [&](int j, auto masked) {
+      constexpr bool M = decltype(masked)::value;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (j < j1) {
+        if (j + 2 < j1) ld.load(K0, Kr, (j + 2) * kBlockN);
+        if (j + 1 < j1) ld.load(V1, Vr, (j + 1) * kBlockN);
+        step<D, DT, CAUSAL, M>(st, cx, j, a0, a1, b0, b1, K1, V0);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (j + 1 < j1) {
+        if (j + 3 < j1) ld.load(K1, Kr, (j + 3) * kBlockN);
+        if (j + 2 < j1) ld.load(V0, Vr, (j + 2) * kBlockN);
+        step<D, DT, CAUSAL, M>(st, cx, j + 1, b0, b1, a0, a1, K0, V1);
+      }
+    };
+    // Unmasked pairs while tile j + 2 needs no bias, then masked pairs.
+    int i = 0;
+    for (; i < pairs && j0 + 2 * i + 2 < tb; ++i) two_steps(j0 + 2 * i, BoolTag<false>{});
+    for (; i < pairs; ++i) two_steps(j0 + 2 * i, BoolTag<true>{});
+  };
+  if (grp == 0) run((lds_t*)ka0, (lds_t*)ka1, (lds_t*)va0, (lds_t*)va1);
+  else run((lds_t*)kb0, (lds_t*)kb1, (lds_t*)vb0, (lds_t*)vb1);
+
+  // Merge: group B publishes, group A combines and stores.
+  if (grp == 1) {
+    xch[rb][0][lane] = st.m2;
+    xch[rb][1][lane] = st.lrun;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[rb][2 + 16 * i + r][lane] = st.oacc[i][r];
+  }
+  __syncthreads();
+  if (grp == 0) {
+    const float mb = xch[rb][0][lane];
+    const float m = fmaxf(st.m2, mb);
+    const float wa = (st.m2 == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(st.m2 - m);
+    const float wb = (mb == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(mb - m);
+    st.m2 = m;
+    st.lrun = wa * st.lrun + wb * xch[rb][1][lane];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.oacc[i][r] = wa * st.oacc[i][r] + wb * xch[rb][2 + 16 * i + r][lane];
+    store_output<D, DT>(p, st, bh, cx.qrow, cx.half);
+  }
+}
+
+// The split-key kernel is available for 16-bit d = 64 and used for grids of
+// kSplitMinGrid to kSplitMaxGrid 128-row query tiles (a grid of a few tiles
+// is bound by launch and load latency, which the split does not shorten).
+template <int D, int DT>
+struct UseSplit {
+  static constexpr bool value = (D == 64 && DT != ATTN_FP8_E4M3);
+};
+constexpr long long kSplitMinGrid = 64;
+constexpr long long kSplitMaxGrid = 512;
+
 // Which loop a (head dim, format) uses: the sequential-step kernel for
 // E4M3 at d = 128, the pipelined one elsewhere.
 template <int D, int DT>
@@ -951,6 +1093,18 @@ int launch_one(const Problem& pr, hipStream_t stream) {
   p.total_tiles = (int)total;
   p.c = pr.scale * kLog2e;
   p.o_scale = pr.v_descale;
+  if constexpr (UseSplit<D, DT>::value) {
+    // Split-key kernel while 128-row query tiles do not fill two rounds of
+    // the 256 CUs (and there are enough of them to be worth splitting).
+    const int n128 = (pr.Nq + 127) / 128;
+    const long long grid = (long long)pr.B * pr.H * n128;
+    if (grid >= kSplitMinGrid && grid <= kSplitMaxGrid) {
+      p.n_qtiles = n128;
+      p.total_tiles = (int)grid;
+      hipLaunchKernelGGL((attn_fwd_split_kernel<D, DT, CAUSAL>), dim3(p.total_tiles), dim3(512), 0, stream, p);
+      return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    }
+  }
   if constexpr (Sequential<D, DT>::value)
     hipLaunchKernelGGL((attn_fwd_seq_kernel<D, DT, CAUSAL>), dim3(p.total_tiles), dim3(64 * kWaves), 0, stream, p);
   else

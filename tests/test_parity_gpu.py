@@ -107,6 +107,26 @@ def test_edge_shapes(nq, nk, causal, d, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d64_split_key_grid(causal, dtype):
+    """d = 64 with 64..512 query tiles of 128 rows and a ragged N: the
+    split-key kernel (two groups walk the two halves of the keys and merge)."""
+    inp = inputs.make(4, 16, 300, 300, 64, dtype, seed=4343 + int(causal), causal=causal)
+    _full_check(inp, f"d64 split-key {'causal' if causal else 'full'} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d64_large_grid(causal, dtype):
+    """d = 64 with more than 512 query tiles of 128 rows: the regular kernel,
+    as for grids of fewer than 64 tiles (the edge shapes); 64..512 tiles take
+    the split-key kernel."""
+    inp = inputs.make(2, 17, 2000, 2000, 64, dtype, seed=4242 + int(causal), causal=causal)
+    _sampled_check(inp, f"d64 large grid {'causal' if causal else 'full'} {dtype}",
+                   heads=[(0, 0), (1, 16)], n_rows=40, seed=5)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_invariants_on_device(dtype):
     B, H, N, d = 2, 3, 333, 128
     inp = inputs.make(B, H, N, N, d, dtype, seed=99)

@@ -1,5 +1,5 @@
 #!/bin/bash
-# rocprofv3 passes behind profiles/attn_fwd_kernel_<WORKLOAD>.md (one MI355X).
+# rocprofv3 passes behind profiles/<kernel>_<WORKLOAD>.md (one MI355X).
 #   bash attention_forward_02_amd/profile_run.sh WORKLOAD OUTDIR
 # Then: python -m attention_forward_02_amd.profiling OUTDIR WORKLOAD
 # Each pass runs under its own time limit and the script stops at the first

@@ -8,7 +8,8 @@ The first command runs, on one MI355X, a kernel trace of the benchmark
 command (`bench.py --no-cpu --workload WORKLOAD`), four counter passes of a
 short benchmark run, and the FETCH_SIZE / WRITE_SIZE passes of a plain
 1 GiB device copy.  The second turns the CSV output into
-`profiles/attn_fwd_kernel_<WORKLOAD>.md` and records the calibrated HBM
+`profiles/<kernel>_<WORKLOAD>.md` (the kernel the workload runs) and
+records the calibrated HBM
 bytes per launch in `profiles/traffic.json`, keyed by workload and stamped
 with the digest of the kernel sources, so `bench.py` reports them only
 while the kernel is the one that was profiled.
@@ -38,7 +39,7 @@ TRAFFIC_JSON = os.path.join(PROFILES, "traffic.json")
 KERNEL_SOURCES = ["csrc/attn_fwd_kernel.h", "csrc/attn_fwd_d64.hip", "csrc/attn_fwd_d128.hip",
                   "csrc/attn_fwd_d256.hip", "csrc/attn_fwd_d64_fp8.hip", "csrc/attn_fwd_d128_fp8.hip",
                   "csrc/attn_fwd_d256_fp8.hip", "csrc/attn_internal.h", "build.py"]
-KERNEL = "attn_fwd_kernel"
+KERNEL = "attn::kernels::attn_fwd"  # every kernel of the library
 N_XCD = 8
 N_SIMD = 1024
 COPY_BYTES = 1 << 30
@@ -104,6 +105,7 @@ def summarize(outdir, workload):
     if len(kern) != 1:
         raise RuntimeError(f"expected one {KERNEL} row in the kernel stats, found {len(kern)}")
     k = kern[0]
+    kname = k["Name"].split("attn::kernels::")[1].split("<")[0]
     avg_ns = float(k["AverageNs"])
     c = {}
     ndisp = {}
@@ -130,7 +132,7 @@ def summarize(outdir, workload):
     cmd_trace = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {outdir}/trace -o run -- "
                  f"python3 bench.py --no-cpu --workload {workload}")
     lines = [
-        f"# {KERNEL} on {workload}",
+        f"# {kname} on {workload}",
         "",
         f"Workload: B={w['B']} H={w['H']} Nq={w['Nq']} Nk={w['Nk']} d={w['d']} "
         f"causal={w['causal']} dtype={w['dtype']}; one launch = {fl:.4g} FLOP.",
@@ -190,7 +192,10 @@ def summarize(outdir, workload):
                      f"{alg_write / 1e6:.1f} MB |")
     lines.append("")
     os.makedirs(PROFILES, exist_ok=True)
-    md = os.path.join(PROFILES, f"{KERNEL}_{workload}.md")
+    md = os.path.join(PROFILES, f"{kname}_{workload}.md")
+    for old in glob.glob(os.path.join(PROFILES, f"*_{workload}.md")):
+        if old != md:
+            os.remove(old)
     with open(md, "w") as f:
         f.write("\n".join(lines))
     try:
@@ -205,6 +210,7 @@ def summarize(outdir, workload):
         "fetch_factor": f_fetch,
         "write_factor": f_write,
         "kernel_digest": kernel_digest(),
+        "kernel": kname,
         "summary": os.path.relpath(md, ROOT),
     }
     with open(TRAFFIC_JSON, "w") as f:

@@ -185,7 +185,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": tr["bytes"] if tr else None,
                      "traffic_unit": "bytes per launch (HBM read + write)",
-                     "kernel": "attn_fwd_kernel", "flops_per_launch": fl},
+                     "kernel": tr["kernel"] if tr else "attn_fwd", "flops_per_launch": fl},
     }
     if not args.no_cpu:
         rec["cpu_baseline"] = _cpu_baseline(inp, args.cpu_seconds)

@@ -1,6 +1,7 @@
 #pragma once
 // Fused attention forward for MI355X (gfx950, CDNA4): device code, shared by
-// one translation unit per head dimension (attn_fwd_d{64,128,256}.hip).
+// one translation unit per head dimension and input format
+// (attn_fwd_d{64,128,256}.hip, attn_fwd_d{64,128,256}_fp8.hip).
 //
 // Computes, per (batch, head), O = softmax(scale * Q K^T) V and the natural
 // log-sum-exp of every score row, one key tile at a time with a running row
@@ -28,14 +29,20 @@
 //   * exp is v_exp_f32 (2^x) on scores pre-multiplied by scale * log2(e);
 //     LSE is converted back to natural log at the end.
 //
-// Schedule (32 query rows per wave; at d <= 128 every SIMD runs two waves,
-// see Waves below): each step overlaps the score
-// MFMAs of the next tile with the exponentials of the current one, and the
-// P V MFMAs with the row sums and the next tile's row max (the pages'
-// two-stage overlap of matrix multiplies and softmax), so the matrix core
-// stays fed from both waves of the SIMD.  Masking is folded into the
-// initial values of the score accumulators, so the step is the same
-// branch-free code for every tile.
+// Three kernels share these pieces:
+//   * attn_fwd_kernel (most shapes): each step overlaps the score MFMAs of
+//     the next tile with the exponentials of the current one, and the P V
+//     MFMAs with the row sums and the next tile's row max (the pages'
+//     two-stage overlap of matrix multiplies and softmax), while the SIMD's
+//     second wave fills the matrix core from its own step;
+//   * attn_fwd_seq_kernel (E4M3, d = 128): the same loop without the
+//     pipelined score tile, for a step bound by softmax VALU work;
+//   * attn_fwd_split_kernel (16-bit d = 64, mid-size grids): two wave groups
+//     walk the two halves of the key range and merge.
+// Masking is folded into the initial values of the score accumulators; the
+// key loops run the unmasked steps and the masked ones (ragged end, causal
+// diagonal) as two loops of one step variant each, so every step is one
+// basic block under one instruction interleave.
 //
 // FP8 E4M3 ("Inside FlashAttention-3", section 5): Q, K, V are E4M3 codes
 // with one descale per tensor.  The q and k descales are folded into the

@@ -28,6 +28,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 from collections import defaultdict
 
@@ -52,12 +53,24 @@ PMC_PASSES = [
 ]
 
 
+def _code_only(rel, text):
+    """Source text without comments and with whitespace collapsed, so that
+    editing a comment does not count as changing the kernel."""
+    if rel.endswith(".py"):
+        text = "\n".join(line.split("#", 1)[0] for line in text.splitlines())
+    else:
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_digest():
-    """sha256 over the kernel's source files and build options."""
+    """sha256 over the code (comments and whitespace aside) of the kernel's
+    source files and build options."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(PKG, rel), "rb") as f:
-            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+        with open(os.path.join(PKG, rel)) as f:
+            h.update(rel.encode() + b"\0" + _code_only(rel, f.read()).encode() + b"\0")
     return h.hexdigest()
 
 
@@ -136,7 +149,7 @@ def summarize(outdir, workload):
         "",
         f"Workload: B={w['B']} H={w['H']} Nq={w['Nq']} Nk={w['Nk']} d={w['d']} "
         f"causal={w['causal']} dtype={w['dtype']}; one launch = {fl:.4g} FLOP.",
-        f"Kernel sources digest: `{kernel_digest()}`",
+        f"Kernel sources digest: `{kernel_digest()}` (code only: comments and whitespace aside)",
         "",
         "Made by (from the repository root, on one MI355X):",
         "",

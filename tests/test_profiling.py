@@ -20,3 +20,12 @@ def test_traffic_follows_kernel_digest(tmp_path, monkeypatch):
 def test_digest_covers_kernel_sources():
     assert len(profiling.kernel_digest()) == 64
     assert "csrc/attn_fwd_kernel.h" in profiling.KERNEL_SOURCES
+
+
+def test_digest_ignores_comments_not_code():
+    src = "int f(int x) {  // doubles\n  return 2 * x; /* a note */\n}\n"
+    assert profiling._code_only("k.h", src) == profiling._code_only("k.h", src.replace("doubles", "twice"))
+    assert profiling._code_only("k.h", src) != profiling._code_only("k.h", src.replace("2 * x", "3 * x"))
+    py = "FLAGS = ['-O3']  # optimise\n"
+    assert profiling._code_only("build.py", py) == profiling._code_only("build.py", py.replace("optimise", "fast"))
+    assert profiling._code_only("build.py", py) != profiling._code_only("build.py", py.replace("-O3", "-O2"))

@@ -26,6 +26,10 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_DTYPE;
   const long long nq = (long long)B * H * Nq * d, nk = (long long)B * H * Nk * d;
   if (nq >= (1LL << 31) || nk >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  // The kernels address one head's K or V block through a buffer resource
+  // with 32-bit byte offsets.
+  const long long head_kv_bytes = (long long)Nk * d * (dtype == ATTN_FP8_E4M3 ? 1 : 2);
+  if (head_kv_bytes >= (1LL << 31)) return ATTN_ERR_SHAPE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return ATTN_ERR_ALIGN;
   const size_t in_elt = dtype == ATTN_FP8_E4M3 ? 1 : 2;
@@ -83,7 +87,8 @@ const char* attn_status_str(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
-    case ATTN_ERR_SHAPE: return "B, H, Nq and Nk must be >= 1 and each tensor < 2^31 elements";
+    case ATTN_ERR_SHAPE:
+      return "B, H, Nq and Nk must be >= 1, each tensor < 2^31 elements and one head's K or V < 2^31 bytes";
     case ATTN_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
     case ATTN_ERR_DTYPE: return "unknown dtype";
     case ATTN_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";

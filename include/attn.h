@@ -61,7 +61,8 @@ typedef enum {
 enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = -1,     /* a required pointer is NULL */
-  ATTN_ERR_SHAPE = -2,    /* B, H, Nq or Nk < 1, or a tensor has >= 2^31 elements */
+  ATTN_ERR_SHAPE = -2,    /* B, H, Nq or Nk < 1, a tensor has >= 2^31 elements, or one
+                             head's K (or V) block, Nk * d * element size, is >= 2^31 bytes */
   ATTN_ERR_HEADDIM = -3,  /* d not in {64, 128, 256} */
   ATTN_ERR_DTYPE = -4,    /* unknown dtype code */
   ATTN_ERR_ALIGN = -5,    /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
@@ -76,7 +77,8 @@ enum {
  * q, k, v  device inputs, layout above, element type `dtype`
  * o, lse   device outputs, layout above (every element is written)
  * B, H     batch size and heads (>= 1)
- * Nq, Nk   query and key counts (>= 1; need not be multiples of any tile)
+ * Nq, Nk   query and key counts (>= 1; need not be multiples of any tile;
+ *          Nk * d * element size < 2^31 bytes)
  * d        head dimension: 64, 128 or 256
  * causal   0 = full attention, nonzero = bottom-right causal mask
  * scale    multiplies Q K^T before the softmax (finite, > 0), e.g. 1/sqrt(d)

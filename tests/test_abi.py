@@ -69,6 +69,11 @@ def _call(**kw):
     (dict(q=None), b.ATTN_ERR_NULL), (dict(k=None), b.ATTN_ERR_NULL), (dict(v=None), b.ATTN_ERR_NULL),
     (dict(o=None), b.ATTN_ERR_NULL), (dict(lse=None), b.ATTN_ERR_NULL),
     (dict(B=0), b.ATTN_ERR_SHAPE), (dict(H=-1), b.ATTN_ERR_SHAPE), (dict(Nq=0), b.ATTN_ERR_SHAPE),
+    # one head's K of 2^22 keys x 256 x 2 B = 2^31 B; one key fewer per tile passes the shape check
+    (dict(H=1, Nk=1 << 22, d=256), b.ATTN_ERR_SHAPE),
+    (dict(H=1, Nk=(1 << 22) - 64, d=256, q=Q + 8), b.ATTN_ERR_ALIGN),
+    (dict(H=1, Nk=1 << 23, d=256, dtype=2), b.ATTN_ERR_SHAPE),
+    (dict(H=1, Nk=(1 << 23) - 64, d=256, dtype=2, q=Q + 8), b.ATTN_ERR_ALIGN),
     (dict(Nk=0), b.ATTN_ERR_SHAPE), (dict(B=1 << 12, H=1 << 10, Nq=1 << 10), b.ATTN_ERR_SHAPE),
     (dict(d=96), b.ATTN_ERR_HEADDIM), (dict(d=32), b.ATTN_ERR_HEADDIM), (dict(d=512), b.ATTN_ERR_HEADDIM),
     (dict(dtype=3), b.ATTN_ERR_DTYPE), (dict(dtype=-1), b.ATTN_ERR_DTYPE),

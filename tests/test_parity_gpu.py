@@ -193,3 +193,36 @@ def test_rejects_invalid_call_on_device():
     from attention_forward_02_amd import ATTN_ERR_HEADDIM, ATTN_ERR_ALIAS
     assert attn_fwd(q, k, v, o, lse, 1, 1, 64, 64, 80, False, 0.125, ATTN_BF16) == ATTN_ERR_HEADDIM
     assert attn_fwd(q, k, v, q, lse, 1, 1, 64, 64, 64, False, 0.125, ATTN_BF16) == ATTN_ERR_ALIAS
+
+
+@pytest.mark.parametrize("dtype,nk", [("bf16", (1 << 22) - 64), ("e4m3", (1 << 23) - 64)])
+def test_largest_head(dtype, nk):
+    # The largest head the library accepts at d = 256 (one head's K and V just
+    # under 2^31 bytes), checked through properties that hold at any size:
+    # Q = 0 makes every score 0, so LSE = ln Nk and O is the mean of V over all
+    # keys; with V = 1, O = 1 up to the rounding of P.
+    d, nq = 256, 64
+    say(f"[gpu] largest head: Nk={nk} d={d} dtype={dtype}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20260 + nk % 97)
+
+    def draw(n):
+        x = torch.randn((1, 1, n, d), generator=gen, device="cuda", dtype=torch.float32).clamp_(-8, 8)
+        return x.to(torch.bfloat16 if dtype == "bf16" else torch.float8_e4m3fn)
+
+    k, v, q = draw(nk), draw(nk), draw(nq)
+    from attention_forward_02_amd import attention
+    desc = (1.0, 1.0, 1.0) if dtype == "e4m3" else None
+    o, lse = attention(torch.zeros_like(q), k, v, causal=False, scale=1.0 / 16, descale=desc)
+    torch.cuda.synchronize()
+    mean_v = v.double().mean(dim=2, keepdim=True).expand(1, 1, nq, d)
+    assert torch.isfinite(o.float()).all()
+    torch.testing.assert_close(o.double(), mean_v, rtol=0, atol=2e-3)
+    torch.testing.assert_close(lse.double(), torch.full_like(lse.double(), float(np.log(nk))), rtol=0, atol=1e-4)
+    del o, lse
+    ones = torch.ones_like(v)
+    o, lse = attention(q, k, ones, causal=False, scale=1.0 / 16, descale=desc)
+    torch.cuda.synchronize()
+    tol = 4e-3 if dtype == "bf16" else 3e-2
+    torch.testing.assert_close(o.double(), torch.ones_like(o.double()), rtol=0, atol=tol)
+    assert torch.isfinite(lse).all()

@@ -6,10 +6,10 @@
 namespace attn {
 namespace kernels {
 
-template __global__ void attn_fwd_kernel<256, ATTN_F16, false>(Params);
-template __global__ void attn_fwd_kernel<256, ATTN_F16, true>(Params);
-template __global__ void attn_fwd_kernel<256, ATTN_BF16, false>(Params);
-template __global__ void attn_fwd_kernel<256, ATTN_BF16, true>(Params);
+template __global__ void attn_fwd_seq_kernel<256, ATTN_F16, false>(Params);
+template __global__ void attn_fwd_seq_kernel<256, ATTN_F16, true>(Params);
+template __global__ void attn_fwd_seq_kernel<256, ATTN_BF16, false>(Params);
+template __global__ void attn_fwd_seq_kernel<256, ATTN_BF16, true>(Params);
 
 }  // namespace kernels
 

@@ -6,8 +6,8 @@
 namespace attn {
 namespace kernels {
 
-template __global__ void attn_fwd_kernel<256, ATTN_FP8_E4M3, false>(Params);
-template __global__ void attn_fwd_kernel<256, ATTN_FP8_E4M3, true>(Params);
+template __global__ void attn_fwd_seq_kernel<256, ATTN_FP8_E4M3, false>(Params);
+template __global__ void attn_fwd_seq_kernel<256, ATTN_FP8_E4M3, true>(Params);
 
 }  // namespace kernels
 

@@ -21,9 +21,15 @@ from .binding import (  # noqa: F401
     ATTN_FP8_E4M3,
     ATTN_OK,
     AttnError,
+    ATTN_FP8_BLOCK_ROWS,
     attention,
+    attention_fp8_blockscaled,
+    attention_fp8_smoothed,
     attn_fwd,
     attn_fwd_fp8,
+    attn_fwd_fp8_blockscaled,
+    attn_quantize_fp8,
     attn_status_str,
     load_library,
+    quantize_fp8,
 )

@@ -1,12 +1,13 @@
 """Thin ctypes binding of libattn.so (argument marshalling only).
 
-The C functions keep their names: ``attn_fwd``, ``attn_fwd_fp8`` and
-``attn_status_str`` take the same arguments as in include/attn.h, with any
-pointer given either as an integer device address or as a torch tensor
-(its ``data_ptr()``), and the stream as a torch stream, an integer handle or
-None (the current torch stream).  ``attention`` is a convenience wrapper that
-allocates the outputs with torch and raises ``AttnError`` on a non-zero
-status.  Every step of the computation runs in the HIP library; if the
+The C functions keep their names: ``attn_fwd``, ``attn_fwd_fp8``,
+``attn_quantize_fp8``, ``attn_fwd_fp8_blockscaled`` and ``attn_status_str``
+take the same arguments as in include/attn.h, with any pointer given either
+as an integer device address or as a torch tensor (its ``data_ptr()``), and
+the stream as a torch stream, an integer handle or None (the current torch
+stream).  ``attention``, ``quantize_fp8``, ``attention_fp8_blockscaled`` and
+``attention_fp8_smoothed`` are convenience wrappers that allocate the
+outputs with torch and raise ``AttnError`` on a non-zero status.  Every step of the computation runs in the HIP library; if the
 library is missing, calls raise instead of falling back to anything else.
 """
 
@@ -16,6 +17,8 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libattn.so")
+
+ATTN_FP8_BLOCK_ROWS = 64
 
 ATTN_F16 = 0
 ATTN_BF16 = 1
@@ -54,6 +57,10 @@ def load_library(path=LIB_PATH):
     lib.attn_fwd.restype = ci
     lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, cf, cf, cf, vp]
     lib.attn_fwd_fp8.restype = ci
+    lib.attn_quantize_fp8.argtypes = [vp, ci, vp, vp, ci, ci, ci, ci, ci, vp]
+    lib.attn_quantize_fp8.restype = ci
+    lib.attn_fwd_fp8_blockscaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
+    lib.attn_fwd_fp8_blockscaled.restype = ci
     lib.attn_status_str.argtypes = [ci]
     lib.attn_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -91,6 +98,22 @@ def attn_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, q_descale, k_d
     return lib.attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
                             int(d), int(bool(causal)), float(scale), float(q_descale), float(k_descale),
                             float(v_descale), _stream(stream))
+
+
+def attn_quantize_fp8(x, dtype, codes, descales, B, H, N, d, hadamard, stream=None):
+    """The C ``attn_quantize_fp8``; returns its status code."""
+    lib = load_library()
+    return lib.attn_quantize_fp8(_ptr(x), int(dtype), _ptr(codes), _ptr(descales), int(B), int(H), int(N), int(d),
+                                 int(bool(hadamard)), _stream(stream))
+
+
+def attn_fwd_fp8_blockscaled(q, k, v, q_descales, k_descales, v_descales, o, lse, B, H, Nq, Nk, d, causal, scale,
+                             stream=None):
+    """The C ``attn_fwd_fp8_blockscaled``; returns its status code."""
+    lib = load_library()
+    return lib.attn_fwd_fp8_blockscaled(_ptr(q), _ptr(k), _ptr(v), _ptr(q_descales), _ptr(k_descales),
+                                        _ptr(v_descales), _ptr(o), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
+                                        int(d), int(bool(causal)), float(scale), _stream(stream))
 
 
 def attn_status_str(status):
@@ -138,3 +161,52 @@ def attention(q, k, v, causal=False, scale=None, descale=None, stream=None):
     if st != ATTN_OK:
         raise AttnError(st)
     return o, lse
+
+
+def quantize_fp8(x, hadamard=False, stream=None):
+    """Block-scaled E4M3 codes of a contiguous fp16/bf16 device tensor x
+    [B,H,N,d]: returns (codes uint8 [B,H,N,d], descales float32
+    [B,H,ceil(N/64)]), optionally after the 16x16 Walsh-Hadamard transform
+    (for Q and K only)."""
+    import torch
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    B, H, N, d = x.shape
+    code = _dtype_code(x)
+    nb = (N + ATTN_FP8_BLOCK_ROWS - 1) // ATTN_FP8_BLOCK_ROWS
+    codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    descales = torch.empty((B, H, nb), dtype=torch.float32, device=x.device)
+    st = attn_quantize_fp8(x, code, codes, descales, B, H, N, d, hadamard, stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return codes, descales
+
+
+def attention_fp8_blockscaled(q, k, v, q_descales, k_descales, v_descales, causal=False, scale=None, stream=None):
+    """O (fp16), LSE for block-scaled E4M3 codes (uint8 or float8_e4m3fn
+    device tensors [B,H,N,d]) and their float32 descales [B,H,ceil(N/64)]."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for t in (q, k, v, q_descales, k_descales, v_descales):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, Nq, d), dtype=torch.float16, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = attn_fwd_fp8_blockscaled(q, k, v, q_descales, k_descales, v_descales, o, lse, B, H, Nq, Nk, d, causal,
+                                  scale, stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return o, lse
+
+
+def attention_fp8_smoothed(q, k, v, causal=False, scale=None, stream=None):
+    """FP8 attention of fp16/bf16 device tensors through block-scaled E4M3:
+    Q and K are quantised after the Walsh-Hadamard transform, V without it,
+    then the block-scaled forward runs.  Returns (O fp16, LSE)."""
+    q8, qd = quantize_fp8(q, True, stream)
+    k8, kd = quantize_fp8(k, True, stream)
+    v8, vd = quantize_fp8(v, False, stream)
+    return attention_fp8_blockscaled(q8, k8, v8, qd, kd, vd, causal, scale, stream)

@@ -46,6 +46,7 @@ SOURCES = [
     ("attn_fwd_d64_fp8.hip", VGPR_FORM),
     ("attn_fwd_d128_fp8.hip", VGPR_FORM),
     ("attn_fwd_d256_fp8.hip", VGPR_FORM),
+    ("attn_quant.hip", []),
 ]
 
 

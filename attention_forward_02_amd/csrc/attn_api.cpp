@@ -64,6 +64,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   p.dtype = dtype;
   p.scale = s;
   p.v_descale = v_ds;
+  p.q_descales = p.k_descales = p.v_descales = nullptr;
   return attn::launch_forward(p, (hipStream_t)stream);
 }
 
@@ -83,6 +84,68 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
              stream);
 }
 
+int attn_quantize_fp8(const void* x, int dtype, void* codes, float* descales, int B, int H, int N, int d,
+                      int hadamard, ihipStream_t* stream) {
+  if (!x || !codes || !descales) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_HEADDIM;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  const long long n = (long long)B * H * N * d;
+  if (n >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(descales, 4)) return ATTN_ERR_ALIGN;
+  const size_t xb = (size_t)n * 2, cb = (size_t)n;
+  const size_t db = (size_t)B * H * ((N + ATTN_FP8_BLOCK_ROWS - 1) / ATTN_FP8_BLOCK_ROWS) * sizeof(float);
+  if (overlap(codes, cb, x, xb) || overlap(descales, db, x, xb) || overlap(descales, db, codes, cb))
+    return ATTN_ERR_ALIAS;
+  attn::QuantProblem p;
+  p.x = x;
+  p.codes = codes;
+  p.descales = descales;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  p.dtype = dtype;
+  p.hadamard = hadamard != 0;
+  return attn::launch_quantize(p, (hipStream_t)stream);
+}
+
+int attn_fwd_fp8_blockscaled(const void* q, const void* k, const void* v, const float* q_descales,
+                             const float* k_descales, const float* v_descales, void* o, float* lse, int B, int H,
+                             int Nq, int Nk, int d, int causal, float scale, ihipStream_t* stream) {
+  int st = validate(q, k, v, o, lse, B, H, Nq, Nk, d, ATTN_FP8_E4M3);
+  if (st != ATTN_OK) return st;
+  if (!q_descales || !k_descales || !v_descales) return ATTN_ERR_NULL;
+  if (!aligned(q_descales, 4) || !aligned(k_descales, 4) || !aligned(v_descales, 4)) return ATTN_ERR_ALIGN;
+  const size_t ob = (size_t)B * H * Nq * d * 2, lb = (size_t)B * H * Nq * sizeof(float);
+  const size_t qdb = (size_t)B * H * ((Nq + ATTN_FP8_BLOCK_ROWS - 1) / ATTN_FP8_BLOCK_ROWS) * sizeof(float);
+  const size_t kdb = (size_t)B * H * ((Nk + ATTN_FP8_BLOCK_ROWS - 1) / ATTN_FP8_BLOCK_ROWS) * sizeof(float);
+  const void* ds[3] = {q_descales, k_descales, v_descales};
+  const size_t dsb[3] = {qdb, kdb, kdb};
+  for (int i = 0; i < 3; ++i)
+    if (overlap(o, ob, ds[i], dsb[i]) || overlap(lse, lb, ds[i], dsb[i])) return ATTN_ERR_ALIAS;
+  if (!positive_finite(scale)) return ATTN_ERR_SCALE;
+  attn::Problem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.d = d;
+  p.causal = causal != 0;
+  p.dtype = ATTN_FP8_E4M3;
+  p.scale = scale;
+  p.v_descale = 1.f;
+  p.q_descales = q_descales;
+  p.k_descales = k_descales;
+  p.v_descales = v_descales;
+  return attn::launch_forward(p, (hipStream_t)stream);
+}
+
 const char* attn_status_str(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
@@ -91,10 +154,11 @@ const char* attn_status_str(int status) {
       return "B, H, Nq and Nk must be >= 1, each tensor < 2^31 elements and one head's K or V < 2^31 bytes";
     case ATTN_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
     case ATTN_ERR_DTYPE: return "unknown dtype";
-    case ATTN_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case ATTN_ERR_ALIGN:
+      return "q, k, v, o (x, codes) must be 16-byte aligned and lse (descales) 4-byte aligned";
     case ATTN_ERR_SCALE: return "scale and descales must be finite and > 0";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
-    case ATTN_ERR_ALIAS: return "o or lse overlaps an input or the other output";
+    case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     default: return "unknown status";
   }
 }

@@ -9,6 +9,9 @@ namespace kernels {
 template __global__ void attn_fwd_seq_kernel<256, ATTN_FP8_E4M3, false>(Params);
 template __global__ void attn_fwd_seq_kernel<256, ATTN_FP8_E4M3, true>(Params);
 
+template __global__ void attn_fwd_seq_kernel<256, ATTN_FP8_E4M3, false, true>(Params);
+template __global__ void attn_fwd_seq_kernel<256, ATTN_FP8_E4M3, true, true>(Params);
+
 }  // namespace kernels
 
 int launch_forward_d256_fp8(const Problem& p, hipStream_t stream) { return kernels::launch_fp8<256>(p, stream); }

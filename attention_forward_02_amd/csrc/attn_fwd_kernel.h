@@ -30,13 +30,15 @@
 //     LSE is converted back to natural log at the end.
 //
 // Three kernels share these pieces:
-//   * attn_fwd_kernel (most shapes): each step overlaps the score MFMAs of
-//     the next tile with the exponentials of the current one, and the P V
-//     MFMAs with the row sums and the next tile's row max (the pages'
-//     two-stage overlap of matrix multiplies and softmax), while the SIMD's
-//     second wave fills the matrix core from its own step;
-//   * attn_fwd_seq_kernel (E4M3, d = 128): the same loop without the
-//     pipelined score tile, for a step bound by softmax VALU work;
+//   * attn_fwd_kernel (16-bit d = 64 and 128, E4M3 d = 64): each step
+//     overlaps the score MFMAs of the next tile with the exponentials of the
+//     current one, and the P V MFMAs with the row sums and the next tile's
+//     row max (the pages' two-stage overlap of matrix multiplies and
+//     softmax), while the SIMD's second wave fills the matrix core from its
+//     own step;
+//   * attn_fwd_seq_kernel (E4M3 d = 128, every d = 256, and the
+//     block-scaled E4M3 variant): the same loop without the pipelined score
+//     tile, for a step bound by softmax VALU work or by registers;
 //   * attn_fwd_split_kernel (16-bit d = 64, mid-size grids): two wave groups
 //     walk the two halves of the key range and merge.
 // Masking is folded into the initial values of the score accumulators; the
@@ -48,7 +50,9 @@
 // with one descale per tensor.  The q and k descales are folded into the
 // score scale and the v descale into the final normalisation; P is rounded
 // to E4M3 (round to nearest even) for the P V product while the row sum
-// uses the unrounded probabilities; O is binary16.
+// uses the unrounded probabilities; O is binary16.  The block-scaled
+// variant (one descale per 64 rows, the same section's block scaling) folds
+// each key tile's K and V descales into that tile's exponent (TileScale).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -94,6 +98,12 @@ struct Params {
   int total_tiles;  // B * H * n_qtiles
   float c;          // scale * log2(e): scores -> base-2 exponent units
   float o_scale;    // multiplies P V (the v descale for E4M3, else 1)
+  // Block-scaled E4M3 only: descales of 64-row blocks, [B*H][nqb] for Q and
+  // [B*H][nkb] for K and V (one K/V block per key tile).
+  const float* qs;
+  const float* ks;
+  const float* vs;
+  int nqb, nkb;
 };
 
 // Input element formats: size and MFMA.
@@ -499,6 +509,18 @@ __device__ __forceinline__ i32x8 pack_p_fp8(const f32x16& p0, const f32x16& p1) 
   return r;
 }
 
+// Scaling of one key tile in the block-scaled E4M3 variant.  A score s of
+// codes is worth 2^(c s) in the softmax (c = scale * log2(e) times the Q and
+// K block descales), and V's block descale vd multiplies the tile's values.
+// Both go into the exponent: p' = 2^(c s + lv - m2) with lv = log2(vd), so
+// the E4M3 P' V product accumulates the descaled values, the reference m2
+// tracks the maximum of c s + lv, and the row sum takes p' / vd = 2^(c s -
+// m2) (iv = 1 / vd).  O / l and m2 + log2 l then come out as with descaled
+// inputs.
+struct TileScale {
+  float c, lv, iv;
+};
+
 // Per-wave constants of the key loop over BN-key tiles.
 template <int BN>
 struct LoopCtxT {
@@ -604,9 +626,7 @@ __device__ __forceinline__ float update_reference(float& m2, float m2t, bool& re
 template <int D, int DT, bool CAUSAL, bool MASKED>
 __device__ __forceinline__ void step(WaveState<D, DT>& st, const LoopCtx& cx, int j, f32x16& s0, f32x16& s1,
                                      f32x16& n0, f32x16& n1, const lds_t* Kn, const lds_t* Vs) {
-  // Phase A.  At d = 256 (one wave per SIMD, so the SIMD's other waves are
-  // the workgroup's own) the wave in its exp-heavy phase gets issue priority.
-  if constexpr (D >= 256) __builtin_amdgcn_s_setprio(1);
+  // Phase A
   masked_scores<D, DT, CAUSAL, MASKED>(st, cx, j + 1, Kn, n0, n1);
   const float mref = (st.m2 == -__builtin_inff()) ? 0.f : st.m2;
 #pragma unroll
@@ -657,7 +677,6 @@ __device__ __forceinline__ void step(WaveState<D, DT>& st, const LoopCtx& cx, in
       st.lrun += (l[0] + l[1]) + (l[2] + l[3]);
     }
   }
-  if constexpr (D >= 256) __builtin_amdgcn_s_setprio(0);
   if constexpr (DT != ATTN_F16) {
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
@@ -846,13 +865,16 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_kernel(Pa
 // would leave one wave per SIMD (d = 256).  K_j and V_j share a ring stage;
 // the loads of tile j + 1 are issued at the start of step j.
 // ---------------------------------------------------------------------------
-template <int D, int DT, bool CAUSAL, bool MASKED, int BN>
+template <int D, int DT, bool CAUSAL, bool MASKED, int BN, bool BS>
 __device__ __forceinline__ void seq_step(WaveState<D, DT>& st, const LoopCtxT<BN>& cx, int j, const lds_t* Kc,
-                                         const lds_t* Vc) {
+                                         const lds_t* Vc, const TileScale& ts) {
   f32x16 s0, s1;
   masked_scores<D, DT, CAUSAL, MASKED>(st, cx, j, Kc, s0, s1);
+  const float c = BS ? ts.c : cx.c;
+  float m2t = tile_max2<BN>(s0, s1, c);
+  if constexpr (BS) m2t += ts.lv;
   bool rescale;
-  const float alpha = update_reference(st.m2, tile_max2<BN>(s0, s1, cx.c), rescale);
+  const float alpha = update_reference(st.m2, m2t, rescale);
   if (rescale) {
     asm volatile("" ::: "memory");  // keep the branch (see step)
     st.lrun *= alpha;
@@ -860,10 +882,11 @@ __device__ __forceinline__ void seq_step(WaveState<D, DT>& st, const LoopCtxT<BN
     for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha;
   }
   const float mref = (st.m2 == -__builtin_inff()) ? 0.f : st.m2;
+  const float off = BS ? ts.lv - mref : -mref;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cx.c, -mref));
-    if constexpr (BN == 64) s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cx.c, -mref));
+    s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, off));
+    if constexpr (BN == 64) s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, off));
   }
   if constexpr (DT == ATTN_FP8_E4M3) {
     pv_tile<D>(st, pack_p_fp8(s0, s1), Vc);
@@ -890,12 +913,15 @@ __device__ __forceinline__ void seq_step(WaveState<D, DT>& st, const LoopCtxT<BN
       ls1 += s1[r + 1];
     }
   }
-  st.lrun += ls0 + ls1;
+  if constexpr (BS) st.lrun = __builtin_fmaf(ls0 + ls1, ts.iv, st.lrun);
+  else st.lrun += ls0 + ls1;
 }
 
-template <int D, int DT, bool CAUSAL>
+// BS: block-scaled E4M3 (per-tile descales, see TileScale).
+template <int D, int DT, bool CAUSAL, bool BS = false>
 __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) __attribute__((amdgpu_waves_per_eu(2)))
 attn_fwd_seq_kernel(Params p) {
+  static_assert(!BS || DT == ATTN_FP8_E4M3, "block scales are an E4M3 variant");
   constexpr int kWaves = Waves<D, DT>::value;
   constexpr int kBlockM = kWaves * kRowsPerWave;
   constexpr int kRowBytes = D * Fmt<DT>::kBytes;
@@ -945,16 +971,42 @@ attn_fwd_seq_kernel(Params p) {
   // each).
   const int tb = min(first_bias_tile<CAUSAL>(cx), nt);
   const int jm = tb & ~1;
+  // Block scales: the wave's 32 rows lie in one 64-row Q block (rows past
+  // Nq take the last block; they are not stored); K/V block j is tile j.
+  // The descales of tile j + 1 are read with that tile's loads, so the
+  // step's vmcnt wait covers them too.
+  float cq = 0.f, kd = 0.f, vd = 0.f;
+  const float* ksh = nullptr;
+  const float* vsh = nullptr;
+  if constexpr (BS) {
+    cq = p.c * p.qs[(size_t)bh * p.nqb + min(cx.qw0 / 64, p.nqb - 1)];
+    ksh = p.ks + (size_t)bh * p.nkb;
+    vsh = p.vs + (size_t)bh * p.nkb;
+    if (nt > 0) {
+      kd = ksh[0];
+      vd = vsh[0];
+    }
+  }
   // Step j: K_j, V_j in (Kc, Vc); tile j + 1 -> (Kl, Vl).
   auto step = [&](int j, const lds_t* Kc, const lds_t* Vc, lds_t* Kl, lds_t* Vl, auto masked) {
     constexpr bool M = decltype(masked)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    TileScale ts{};
+    if constexpr (BS) {
+      ts.c = cq * kd;
+      ts.lv = __builtin_amdgcn_logf(vd);
+      ts.iv = __builtin_amdgcn_rcpf(vd);
+    }
     __syncthreads();
     if (j + 1 < nt) {
       ld.load(Kl, Kr, (j + 1) * BN);
       ld.load(Vl, Vr, (j + 1) * BN);
+      if constexpr (BS) {
+        kd = ksh[j + 1];
+        vd = vsh[j + 1];
+      }
     }
-    seq_step<D, DT, CAUSAL, M, BN>(st, cx, j, Kc, Vc);
+    seq_step<D, DT, CAUSAL, M, BN, BS>(st, cx, j, Kc, Vc, ts);
   };
   int j = 0;
   for (; j < jm; j += 2) {
@@ -1142,6 +1194,8 @@ int launch_one(const Problem& pr, hipStream_t stream) {
   p.total_tiles = (int)total;
   p.c = pr.scale * kLog2e;
   p.o_scale = pr.v_descale;
+  p.qs = p.ks = p.vs = nullptr;
+  p.nqb = p.nkb = 0;
   if constexpr (UseSplit<D, DT>::value) {
     // Split-key kernel while 128-row query tiles do not fill two rounds of
     // the 256 CUs (and there are enough of them to be worth splitting).
@@ -1174,10 +1228,43 @@ int launch_16bit(const Problem& p, hipStream_t s) {
   }
 }
 
+// Block-scaled E4M3: always the sequential kernel, whose steps take one
+// key tile (= one K/V block) at a time.
+template <int D, bool CAUSAL>
+int launch_blockscaled(const Problem& pr, hipStream_t stream) {
+  constexpr int kWaves = Waves<D, ATTN_FP8_E4M3>::value;
+  constexpr int kBlockM = kWaves * kRowsPerWave;
+  static_assert(TileKeys<D, ATTN_FP8_E4M3>::value == ATTN_FP8_BLOCK_ROWS, "one K/V block per key tile");
+  Params p;
+  p.q = (const unsigned char*)pr.q;
+  p.k = (const unsigned char*)pr.k;
+  p.v = (const unsigned char*)pr.v;
+  p.o = (uint16_t*)pr.o;
+  p.lse = pr.lse;
+  p.Nq = pr.Nq;
+  p.Nk = pr.Nk;
+  p.n_qtiles = (pr.Nq + kBlockM - 1) / kBlockM;
+  const long long total = (long long)pr.B * pr.H * p.n_qtiles;
+  if (total > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  p.total_tiles = (int)total;
+  p.c = pr.scale * kLog2e;
+  p.o_scale = 1.f;
+  p.qs = pr.q_descales;
+  p.ks = pr.k_descales;
+  p.vs = pr.v_descales;
+  p.nqb = (pr.Nq + ATTN_FP8_BLOCK_ROWS - 1) / ATTN_FP8_BLOCK_ROWS;
+  p.nkb = (pr.Nk + ATTN_FP8_BLOCK_ROWS - 1) / ATTN_FP8_BLOCK_ROWS;
+  hipLaunchKernelGGL((attn_fwd_seq_kernel<D, ATTN_FP8_E4M3, CAUSAL, true>), dim3(p.total_tiles), dim3(64 * kWaves),
+                     0, stream, p);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 // E4M3, one head dimension.
 template <int D>
 int launch_fp8(const Problem& p, hipStream_t s) {
   if (p.dtype != ATTN_FP8_E4M3) return ATTN_ERR_DTYPE;
+  if (p.q_descales)
+    return p.causal ? launch_blockscaled<D, true>(p, s) : launch_blockscaled<D, false>(p, s);
   return p.causal ? launch_one<D, ATTN_FP8_E4M3, true>(p, s) : launch_one<D, ATTN_FP8_E4M3, false>(p, s);
 }
 

@@ -1,5 +1,5 @@
 // Private interface between the C ABI (attn_api.cpp) and the kernels
-// (attn_fwd.hip).  Not installed; not part of the public header.
+// (attn_fwd_d*.hip, attn_quant.hip).  Not installed; not part of the public header.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,9 +18,27 @@ struct Problem {
   int dtype;          // attn_dtype
   float scale;        // multiplies Q K^T (dequantisation of q and k folded in for fp8)
   float v_descale;    // multiplies P V (1 unless fp8)
+  // Block-scaled E4M3 (attn_fwd_fp8_blockscaled): one descale per
+  // ATTN_FP8_BLOCK_ROWS rows of each head, [B][H][ceil(N / rows)]; NULL
+  // otherwise.  `scale` then excludes the descales.
+  const float* q_descales;
+  const float* k_descales;
+  const float* v_descales;
 };
 
 // Launches the forward pass on `stream`.  Returns 0 or a negative ATTN_ERR_*.
 int launch_forward(const Problem& p, hipStream_t stream);
+
+// One tensor's block-scaled E4M3 quantisation, validated by the C ABI.
+struct QuantProblem {
+  const void* x;      // [B][H][N][d] binary16 or bfloat16
+  void* codes;        // [B][H][N][d] E4M3 codes
+  float* descales;    // [B][H][ceil(N / ATTN_FP8_BLOCK_ROWS)]
+  int B, H, N, d;
+  int dtype;          // ATTN_F16 or ATTN_BF16
+  int hadamard;       // nonzero: 16x16 Walsh-Hadamard transform first
+};
+
+int launch_quantize(const QuantProblem& p, hipStream_t stream);
 
 }  // namespace attn

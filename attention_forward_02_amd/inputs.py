@@ -8,22 +8,26 @@ code that both the HIP path's callers and the CPU oracle's callers share.
 
 Workloads (all inputs i.i.d. N(0, 1) float32, scale = fp32(1/sqrt(d))):
 
-=====================  ==  ==  =====  =====  ===  ======  =====
-name                   B   H   Nq     Nk     d    causal  dtype
-=====================  ==  ==  =====  =====  ===  ======  =====
-tiny_d64_f16           1   1   128    128    64   no      f16
-causal_d64_bf16        4   8   1024   1024   64   yes     bf16
-hd128_seq8k_f16        2   16  8192   8192   128  no      f16
-causal_d256_bf16       1   16  16384  16384  256  yes     bf16
-hd128_seq8k_e4m3       2   16  8192   8192   128  no      e4m3
-=====================  ==  ==  =====  =====  ===  ======  =====
+==========================  ==  ==  =====  =====  ===  ======  =====
+name                        B   H   Nq     Nk     d    causal  dtype
+==========================  ==  ==  =====  =====  ===  ======  =====
+tiny_d64_f16                1   1   128    128    64   no      f16
+causal_d64_bf16             4   8   1024   1024   64   yes     bf16
+hd128_seq8k_f16             2   16  8192   8192   128  no      f16
+causal_d256_bf16            1   16  16384  16384  256  yes     bf16
+hd128_seq8k_e4m3            2   16  8192   8192   128  no      e4m3
+hd128_seq8k_e4m3_smoothed   2   16  8192   8192   128  no      f16
+==========================  ==  ==  =====  =====  ===  ======  =====
 
 ``hd128_seq8k_f16`` is the head-dim-128, sequence-8192 FP16 shape of the
 pingpong measurement reported for FlashAttention-3 (Warp-specialization
 concept card, "Pingpong scheduling between two consumer warpgroups").  The
 e4m3 workload adds 0.1% outliers (entries multiplied by 20) to every tensor
 before per-tensor quantisation, the situation the FP8 section of "Inside
-FlashAttention-3" (section 5) targets.
+FlashAttention-3" (section 5) targets.  ``hd128_seq8k_e4m3_smoothed``
+draws the same float32 values (same seed) but hands them over as binary16:
+its path quantises them on the GPU itself, block-scaled, with Q and K
+Walsh-Hadamard-smoothed first (the second FP8 item of that section).
 """
 
 from dataclasses import dataclass, field
@@ -40,6 +44,8 @@ WORKLOADS = {
     "causal_d256_bf16": dict(B=1, H=16, Nq=16384, Nk=16384, d=256, causal=True, dtype="bf16", seed=1004),
     "hd128_seq8k_e4m3": dict(B=2, H=16, Nq=8192, Nk=8192, d=128, causal=False, dtype="e4m3",
                              seed=1005, outliers=True),
+    "hd128_seq8k_e4m3_smoothed": dict(B=2, H=16, Nq=8192, Nk=8192, d=128, causal=False, dtype="f16",
+                                      seed=1005, outliers=True, smoothed=True),
 }
 
 E4M3_MAX = 448.0

@@ -39,7 +39,8 @@ TRAFFIC_JSON = os.path.join(PROFILES, "traffic.json")
 
 KERNEL_SOURCES = ["csrc/attn_fwd_kernel.h", "csrc/attn_fwd_d64.hip", "csrc/attn_fwd_d128.hip",
                   "csrc/attn_fwd_d256.hip", "csrc/attn_fwd_d64_fp8.hip", "csrc/attn_fwd_d128_fp8.hip",
-                  "csrc/attn_fwd_d256_fp8.hip", "csrc/attn_internal.h", "build.py"]
+                  "csrc/attn_fwd_d256_fp8.hip", "csrc/attn_quant.hip", "csrc/attn_internal.h",
+                  "build.py"]
 KERNEL = "attn::kernels::attn_fwd"  # every kernel of the library
 N_XCD = 8
 N_SIMD = 1024
@@ -138,7 +139,7 @@ def summarize(outdir, workload):
     mfma_busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_SIMD)
     lds_conf = c["SQ_LDS_BANK_CONFLICT"] / max(1.0, c["SQ_LDS_IDX_ACTIVE"])
     fl = inputs.flops(w["B"], w["H"], w["Nq"], w["Nk"], w["d"], w["causal"])
-    elt = 1 if w["dtype"] == "e4m3" else 2
+    elt = 1 if w["dtype"] == "e4m3" or w.get("smoothed") else 2
     alg_read = 3 * w["B"] * w["H"] * w["Nq"] * w["d"] * elt if w["Nq"] == w["Nk"] else None
     alg_write = w["B"] * w["H"] * w["Nq"] * (w["d"] * 2 + 4)
     tflops = fl / (avg_ns * 1e-9) / 1e12
@@ -169,6 +170,16 @@ def summarize(outdir, workload):
         f"| `{k['Name']}` | {k['Calls']} | {avg_ns:.0f} | {float(k['MinNs']):.0f} | {float(k['MaxNs']):.0f} "
         f"| {tflops:.1f} |",
         "",
+    ]
+    others = [r for r in stats_rows if KERNEL not in r["Name"] and "attn::" in r["Name"]]
+    if others:
+        lines += ["Other kernels of the same step:", "",
+                  "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+        for r in others:
+            lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {float(r['MinNs']):.0f} "
+                         f"| {float(r['MaxNs']):.0f} |")
+        lines.append("")
+    lines += [
         "## Counters (`--pmc`, one pass each, per dispatch)",
         "",
         "```",

@@ -4,9 +4,13 @@
 
 A step is one attn_fwd call over the whole workload (default: B=2, H=16,
 Nq=Nk=8192, d=128, non-causal fp16), inputs resident in HBM before timing.
+For the smoothed FP8 workload a step is the whole path from binary16
+inputs: three block-scaled E4M3 quantisations (Q and K Walsh-Hadamard
+smoothed) and the block-scaled forward.
 Prints ONE JSON line with TFLOP/s (4*B*H*Nq*Nk*d, halved for causal), the
-MFMA roofline of the kernel, and the float64 CPU oracle timed on a bounded
-sample of the same workload on this machine's host cores.
+MFMA roofline of the attention kernel (its own launch time, from HIP events
+around its launches), and the float64 CPU oracle timed on a bounded sample
+of the same workload on this machine's host cores.
 """
 
 import argparse
@@ -27,9 +31,10 @@ METRIC = "attention fwd TFLOPs/s and % of MFMA peak, hdim128 seq8192 fp16, 1 GPU
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2}
 
 
-def _cpu_baseline(inp, budget_s):
+def _cpu_baseline(inp, budget_s, smoothed=False):
     """Time the oracle (as it stands) on whole 512-row query chunks of the
-    workload's heads, in order, until about `budget_s` seconds of CPU work."""
+    workload's heads, in order, until about `budget_s` seconds of CPU work
+    (for the smoothed FP8 workload including the quantisation of each head)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -38,6 +43,10 @@ def _cpu_baseline(inp, budget_s):
         threads = len(os.sched_getaffinity(0))
     dec = {"f16": oracle.decode_f16, "bf16": oracle.decode_bf16, "e4m3": oracle.decode_e4m3}[inp.dtype]
     qd, kd, vd = (float(x) for x in inp.descale)
+    if smoothed:
+        # the oracle's block-scaled quantisation of the head, timed with it
+        def dec_q(bits, had):
+            return oracle.dequantize_blocks(*oracle.quantize_blocks(oracle.decode_f16(bits), had))
     chunk = 512
     flops = 0.0
     spent = 0.0
@@ -45,9 +54,16 @@ def _cpu_baseline(inp, budget_s):
     heads = 0
     for b in range(inp.B):
         for h in range(inp.H):
-            q = dec(inp.q[b, h])[None, None] * qd
-            k = dec(inp.k[b, h])[None, None] * kd
-            v = dec(inp.v[b, h])[None, None] * vd
+            if smoothed:
+                t0 = time.perf_counter()
+                q = dec_q(inp.q[b, h][None, None], True)
+                k = dec_q(inp.k[b, h][None, None], True)
+                v = dec_q(inp.v[b, h][None, None], False)
+                spent += time.perf_counter() - t0
+            else:
+                q = dec(inp.q[b, h])[None, None] * qd
+                k = dec(inp.k[b, h])[None, None] * kd
+                v = dec(inp.v[b, h])[None, None] * vd
             heads += 1
             for r0 in range(0, inp.Nq, chunk):
                 rows = np.arange(r0, min(inp.Nq, r0 + chunk))
@@ -72,7 +88,8 @@ def _cpu_baseline(inp, budget_s):
         "cores": int(threads),
         "kind": "oracle",
         "sample": (f"{done_rows} query rows ({chunk}-row chunks) of {heads} of {inp.B * inp.H} heads, "
-                   f"{spent:.1f} s, float64 numpy oracle, same FLOP count convention"),
+                   f"{spent:.1f} s, float64 numpy oracle, same FLOP count convention"
+                   + (", plus the oracle's block-scaled quantisation of those heads" if smoothed else "")),
     }
 
 
@@ -119,9 +136,11 @@ def main():
         _copy_calibration(torch, args)
         return
     from attention_forward_02_amd import inputs
-    from attention_forward_02_amd.binding import attn_fwd, attn_fwd_fp8, ATTN_F16, ATTN_BF16, ATTN_OK, AttnError
+    from attention_forward_02_amd.binding import (attn_fwd, attn_fwd_fp8, attn_fwd_fp8_blockscaled, attn_quantize_fp8,
+                                                  ATTN_F16, ATTN_BF16, ATTN_FP8_BLOCK_ROWS, ATTN_OK, AttnError)
 
     w = inputs.WORKLOADS[args.workload]
+    smoothed = bool(w.get("smoothed", False))
     inp = inputs.make_workload(args.workload)
     dev = torch.device("cuda:0")
 
@@ -136,16 +155,41 @@ def main():
     lse = torch.empty((inp.B, inp.H, inp.Nq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     code = {"f16": ATTN_F16, "bf16": ATTN_BF16}.get(inp.dtype)
+    if smoothed:
+        nqb = -(-inp.Nq // ATTN_FP8_BLOCK_ROWS)
+        nkb = -(-inp.Nk // ATTN_FP8_BLOCK_ROWS)
+        q8, k8, v8 = (torch.empty(t.shape, dtype=torch.uint8, device=dev) for t in (q, k, v))
+        qs = torch.empty((inp.B, inp.H, nqb), dtype=torch.float32, device=dev)
+        ks, vs = (torch.empty((inp.B, inp.H, nkb), dtype=torch.float32, device=dev) for _ in range(2))
+    # HIP events around every attention launch of the timed steps (on the
+    # stream the kernels run on): the attention kernel's own duration.
+    marks = []
 
-    def step():
-        if inp.dtype == "e4m3":
+    def check(st):
+        if st != ATTN_OK:
+            raise AttnError(st)
+
+    def step(timed=False):
+        if smoothed:
+            check(attn_quantize_fp8(q, ATTN_F16, q8, qs, inp.B, inp.H, inp.Nq, inp.d, True, stream))
+            check(attn_quantize_fp8(k, ATTN_F16, k8, ks, inp.B, inp.H, inp.Nk, inp.d, True, stream))
+            check(attn_quantize_fp8(v, ATTN_F16, v8, vs, inp.B, inp.H, inp.Nk, inp.d, False, stream))
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        if smoothed:
+            st = attn_fwd_fp8_blockscaled(q8, k8, v8, qs, ks, vs, o, lse, inp.B, inp.H, inp.Nq, inp.Nk, inp.d,
+                                          inp.causal, float(inp.scale), stream)
+        elif inp.dtype == "e4m3":
             st = attn_fwd_fp8(q, k, v, o, lse, inp.B, inp.H, inp.Nq, inp.Nk, inp.d, inp.causal, float(inp.scale),
                               *(float(x) for x in inp.descale), stream)
         else:
             st = attn_fwd(q, k, v, o, lse, inp.B, inp.H, inp.Nq, inp.Nk, inp.d, inp.causal, float(inp.scale),
                           code, stream)
-        if st != ATTN_OK:
-            raise AttnError(st)
+        check(st)
+        if timed:
+            e1.record(stream)
+            marks.append((e0, e1))
 
     for _ in range(args.warmup):
         step()
@@ -154,14 +198,17 @@ def main():
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(args.steps):
-        step()
+        step(timed=True)
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    kernel_ms = sum(a.elapsed_time(b) for a, b in marks) / len(marks)
 
     fl = inputs.flops(inp.B, inp.H, inp.Nq, inp.Nk, inp.d, inp.causal)
     tflops = fl / (ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[inp.dtype]
+    kernel_tflops = fl / (kernel_ms * 1e-3) / 1e12
+    mma_dtype = "e4m3" if smoothed else inp.dtype
+    peak = PEAK_TFLOPS[mma_dtype]
     # HBM bytes per launch from the committed rocprofv3 counter passes
     # (FETCH_SIZE + WRITE_SIZE, copy-calibrated); None once the kernel
     # sources differ from the ones profiled.
@@ -178,17 +225,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": inp.dtype,
-        "data": "synthetic: seeded i.i.d. N(0,1) inputs",
+        "dtype": mma_dtype,
+        "data": "synthetic: seeded i.i.d. N(0,1) inputs" + (" with 0.1% x20 outliers" if w.get("outliers") else ""),
         "config": {"workload": args.workload, "B": inp.B, "H": inp.H, "Nq": inp.Nq, "Nk": inp.Nk, "d": inp.d,
                    "causal": inp.causal, "in_dtype": inp.dtype, "flops_per_step": fl},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": tr["bytes"] if tr else None,
+        "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(kernel_tflops / peak, 4), "traffic": tr["bytes"] if tr else None,
                      "traffic_unit": "bytes per launch (HBM read + write)",
-                     "kernel": tr["kernel"] if tr else "attn_fwd", "flops_per_launch": fl},
+                     "kernel": tr["kernel"] if tr else "attn_fwd", "flops_per_launch": fl,
+                     "kernel_ms": round(kernel_ms, 4)},
     }
+    if smoothed:
+        rec["config"]["path"] = ("block-scaled E4M3, 64-row blocks; Q and K 16x16 Walsh-Hadamard smoothed; "
+                                 "quantisation of Q, K, V inside the step")
     if not args.no_cpu:
-        rec["cpu_baseline"] = _cpu_baseline(inp, args.cpu_seconds)
+        rec["cpu_baseline"] = _cpu_baseline(inp, args.cpu_seconds, smoothed)
     print(json.dumps(rec), flush=True)
 
 

@@ -15,7 +15,9 @@
  * memory yields the output block and one log-sum-exp per row, returned as
  * (output / row_sum, row_max + log(row_sum)).  The FP8 E4M3 variant with
  * per-tensor scaling is section 5 of "Inside FlashAttention-3 &
- * Warp-Specialized CUDA Kernels" (tekromancy.com).  The pages describe one
+ * Warp-Specialized CUDA Kernels" (tekromancy.com), and so is the
+ * block-scaled variant with 16x16 Walsh-Hadamard smoothing of Q and K
+ * (attn_quantize_fp8 + attn_fwd_fp8_blockscaled).  The pages describe one
  * key/value tile stream per (batch, head) of a (B, H, N, D) tensor.
  *
  * Layout (all tensors dense, row-major, innermost dimension contiguous):
@@ -52,6 +54,11 @@ extern "C" {
 /* Same type as HIP's hipStream_t. */
 struct ihipStream_t;
 
+/* Rows per quantisation block of the block-scaled FP8 variant: each
+ * (batch, head) of a tensor is cut into blocks of this many consecutive rows
+ * (the last one may be shorter), each with its own float32 descale. */
+#define ATTN_FP8_BLOCK_ROWS 64
+
 typedef enum {
   ATTN_F16 = 0,       /* IEEE binary16 in, binary16 out */
   ATTN_BF16 = 1,      /* bfloat16 in, bfloat16 out */
@@ -65,10 +72,11 @@ enum {
                              head's K (or V) block, Nk * d * element size, is >= 2^31 bytes */
   ATTN_ERR_HEADDIM = -3,  /* d not in {64, 128, 256} */
   ATTN_ERR_DTYPE = -4,    /* unknown dtype code */
-  ATTN_ERR_ALIGN = -5,    /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
+  ATTN_ERR_ALIGN = -5,    /* q, k, v, o (x, codes) not 16-byte aligned, or lse (descales)
+                             not 4-byte aligned */
   ATTN_ERR_SCALE = -6,    /* scale or a descale is not finite and > 0 */
   ATTN_ERR_LAUNCH = -7,   /* the kernel launch failed */
-  ATTN_ERR_ALIAS = -8     /* o or lse overlaps an input or the other output */
+  ATTN_ERR_ALIAS = -8     /* an output overlaps an input or another output */
 };
 
 /*
@@ -102,6 +110,63 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int H, int Nq, int Nk, int d, int causal, float scale,
                  float q_descale, float k_descale, float v_descale,
                  struct ihipStream_t* stream);
+
+/*
+ * attn_quantize_fp8: block-scaled FP8 E4M3 quantisation of one attention
+ * input, optionally after a 16x16 Walsh-Hadamard transform ("Inside
+ * FlashAttention-3", section 5, block scaling with Hadamard outlier
+ * smoothing).  With `hadamard` nonzero every group of 16 consecutive
+ * channels of a row is multiplied by H/4, H the Sylvester-ordered 16x16
+ * Walsh-Hadamard matrix (entry (i, j) = (-1)^popcount(i & j)); H/4 is
+ * orthogonal, so applying it to both Q and K leaves Q K^T unchanged.  Use
+ * it for Q and K, never for V.
+ *
+ * Per block of ATTN_FP8_BLOCK_ROWS rows of one (batch, head), with y the
+ * (transformed) values rounded once to float32:
+ *   descale = amax|y| / 448 in IEEE float32 (1 if the block is all zero)
+ *   code    = E4M3 round-to-nearest-even of (y / descale), float32 division
+ * so that code * descale approximates y.
+ *
+ * x         device input [B][H][N][d], binary16 (ATTN_F16) or bfloat16
+ *           (ATTN_BF16), finite values, 16-byte aligned
+ * dtype     ATTN_F16 or ATTN_BF16
+ * codes     device output [B][H][N][d] E4M3 codes, 16-byte aligned
+ * descales  device output [B][H][ceil(N / ATTN_FP8_BLOCK_ROWS)] float32,
+ *           4-byte aligned
+ * B, H, N   >= 1; d is 64, 128 or 256; B*H*N*d < 2^31
+ * hadamard  nonzero: transform before quantising
+ * stream    HIP stream to enqueue on (NULL = default stream)
+ *
+ * codes and descales must not overlap x or each other (ATTN_ERR_ALIAS).
+ * Returns ATTN_OK or a negative ATTN_ERR_* code, as attn_fwd.
+ */
+int attn_quantize_fp8(const void* x, int dtype, void* codes, float* descales,
+                      int B, int H, int N, int d, int hadamard,
+                      struct ihipStream_t* stream);
+
+/*
+ * attn_fwd_fp8_blockscaled: the FP8 E4M3 forward with one descale per block
+ * of ATTN_FP8_BLOCK_ROWS rows, as attn_quantize_fp8 produces them.  The real
+ * value of an element of q (k, v) in row r of head (b, h) is its code times
+ * q_descales[(b*H + h)*nq + r / ATTN_FP8_BLOCK_ROWS] with nq = ceil(Nq /
+ * ATTN_FP8_BLOCK_ROWS) (nk = ceil(Nk / ATTN_FP8_BLOCK_ROWS) for k and v).
+ * If q and k were quantised after the Walsh-Hadamard transform, the scores,
+ * and so O and LSE, are those of the untransformed inputs up to rounding.
+ *
+ * q, k, v          device E4M3 codes, layout above, 16-byte aligned
+ * q_descales       device float32 [B][H][nq]; k_descales, v_descales
+ *                  [B][H][nk]; 4-byte aligned; every value finite and > 0
+ *                  (not checked: they live in device memory)
+ * o, lse, B, H, Nq, Nk, d, causal, scale, stream: as attn_fwd; o is binary16
+ *
+ * o and lse must not overlap any input, descale array or each other.
+ * Returns ATTN_OK or a negative ATTN_ERR_* code.
+ */
+int attn_fwd_fp8_blockscaled(const void* q, const void* k, const void* v,
+                             const float* q_descales, const float* k_descales,
+                             const float* v_descales, void* o, float* lse,
+                             int B, int H, int Nq, int Nk, int d, int causal,
+                             float scale, struct ihipStream_t* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_str(int status);

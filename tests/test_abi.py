@@ -28,7 +28,8 @@ def _declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert set(_declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_status_str"}
+    assert set(_declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_fwd_fp8_blockscaled",
+                                          "attn_status_str"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -96,6 +97,50 @@ def test_fp8_descales_validated():
         assert st == b.ATTN_ERR_SCALE
     st = lib.attn_fwd_fp8(None, a["k"], a["v"], a["o"], a["lse"], 1, 2, 128, 128, 64, 0, 0.125, 1.0, 1.0, 1.0, None)
     assert st == b.ATTN_ERR_NULL
+
+
+def test_block_rows_match_header():
+    src = open(HEADER).read()
+    assert int(re.search(r"#define ATTN_FP8_BLOCK_ROWS (\d+)", src).group(1)) == b.ATTN_FP8_BLOCK_ROWS == 64
+
+
+X, C, DS = 0x10000000, 0x20000000, 0x30000000
+QGOOD = dict(x=X, dtype=0, codes=C, descales=DS, B=2, H=3, N=100, d=128, hadamard=1)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), b.ATTN_ERR_NULL), (dict(codes=None), b.ATTN_ERR_NULL), (dict(descales=None), b.ATTN_ERR_NULL),
+    (dict(B=0), b.ATTN_ERR_SHAPE), (dict(N=0), b.ATTN_ERR_SHAPE), (dict(H=-2), b.ATTN_ERR_SHAPE),
+    (dict(B=1 << 10, H=1 << 10, N=1 << 10), b.ATTN_ERR_SHAPE),
+    (dict(d=96), b.ATTN_ERR_HEADDIM), (dict(dtype=2), b.ATTN_ERR_DTYPE), (dict(dtype=7), b.ATTN_ERR_DTYPE),
+    (dict(x=X + 8), b.ATTN_ERR_ALIGN), (dict(codes=C + 4), b.ATTN_ERR_ALIGN), (dict(descales=DS + 2), b.ATTN_ERR_ALIGN),
+    (dict(codes=X + 1024), b.ATTN_ERR_ALIAS), (dict(descales=C + 64), b.ATTN_ERR_ALIAS),
+    (dict(descales=X + 2 * 2 * 3 * 100 * 128 - 4), b.ATTN_ERR_ALIAS),
+])
+def test_quantize_validation_rejects_before_launch(kw, code):
+    a = dict(QGOOD)
+    a.update(kw)
+    st = _lib().attn_quantize_fp8(a["x"], a["dtype"], a["codes"], a["descales"], a["B"], a["H"], a["N"], a["d"],
+                                  a["hadamard"], None)
+    assert st == code
+
+
+QS, KS, VS = 0x60000000, 0x61000000, 0x62000000
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qs=None), b.ATTN_ERR_NULL), (dict(ks=None), b.ATTN_ERR_NULL), (dict(vs=None), b.ATTN_ERR_NULL),
+    (dict(q=None), b.ATTN_ERR_NULL), (dict(d=80), b.ATTN_ERR_HEADDIM), (dict(Nk=0), b.ATTN_ERR_SHAPE),
+    (dict(qs=QS + 2), b.ATTN_ERR_ALIGN), (dict(vs=VS + 1), b.ATTN_ERR_ALIGN), (dict(q=Q + 4), b.ATTN_ERR_ALIGN),
+    (dict(qs=O + 4096), b.ATTN_ERR_ALIAS), (dict(ks=L), b.ATTN_ERR_ALIAS), (dict(o=V), b.ATTN_ERR_ALIAS),
+    (dict(scale=0.0), b.ATTN_ERR_SCALE), (dict(scale=float("nan")), b.ATTN_ERR_SCALE),
+])
+def test_blockscaled_validation_rejects_before_launch(kw, code):
+    a = dict(q=Q, k=K, v=V, qs=QS, ks=KS, vs=VS, o=O, lse=L, B=1, H=2, Nq=128, Nk=128, d=64, causal=0, scale=0.125)
+    a.update(kw)
+    st = _lib().attn_fwd_fp8_blockscaled(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"],
+                                         a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], None)
+    assert st == code
 
 
 def test_binding_raises_without_library(tmp_path):

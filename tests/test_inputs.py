@@ -40,7 +40,11 @@ def test_workloads_are_seeded_and_shaped():
     tiny = inputs.make_workload("tiny_d64_f16")
     assert tiny.q.shape == (1, 1, 128, 64) and not tiny.causal
     assert set(inputs.WORKLOADS) == {"tiny_d64_f16", "causal_d64_bf16", "hd128_seq8k_f16",
-                                     "causal_d256_bf16", "hd128_seq8k_e4m3"}
+                                     "causal_d256_bf16", "hd128_seq8k_e4m3", "hd128_seq8k_e4m3_smoothed"}
+    # the smoothed FP8 workload draws the same float32 values as the per-tensor one
+    a = inputs.make(1, 1, 64, 64, 128, "e4m3", seed=5, outliers=True, keep_f32=True)
+    b = inputs.make(1, 1, 64, 64, 128, "f16", seed=5, outliers=True, keep_f32=True)
+    assert np.array_equal(a.q32, b.q32) and np.array_equal(a.v32, b.v32)
 
 
 def test_outliers_are_present():

@@ -17,9 +17,16 @@ from .binding import (  # noqa: F401
     ATTN_ERR_NULL,
     ATTN_ERR_SCALE,
     ATTN_ERR_SHAPE,
+    ATTN_ERR_VARIANT,
     ATTN_F16,
     ATTN_FP8_E4M3,
     ATTN_OK,
+    ATTN_VARIANT_AUTO,
+    ATTN_VARIANT_PIPELINED,
+    ATTN_VARIANT_PIPELINED_4STAGE,
+    ATTN_VARIANT_SEQUENTIAL,
+    ATTN_VARIANT_SPLIT,
+    VARIANT_NAMES,
     AttnError,
     ATTN_FP8_BLOCK_ROWS,
     attention,
@@ -28,8 +35,10 @@ from .binding import (  # noqa: F401
     attn_fwd,
     attn_fwd_fp8,
     attn_fwd_fp8_blockscaled,
+    attn_fwd_variant,
     attn_quantize_fp8,
     attn_status_str,
+    attn_variant_available,
     load_library,
     quantize_fp8,
 )

@@ -1,7 +1,8 @@
 """Thin ctypes binding of libattn.so (argument marshalling only).
 
 The C functions keep their names: ``attn_fwd``, ``attn_fwd_fp8``,
-``attn_quantize_fp8``, ``attn_fwd_fp8_blockscaled`` and ``attn_status_str``
+``attn_fwd_variant``, ``attn_variant_available``, ``attn_quantize_fp8``,
+``attn_fwd_fp8_blockscaled`` and ``attn_status_str``
 take the same arguments as in include/attn.h, with any pointer given either
 as an integer device address or as a torch tensor (its ``data_ptr()``), and
 the stream as a torch stream, an integer handle or None (the current torch
@@ -33,6 +34,16 @@ ATTN_ERR_ALIGN = -5
 ATTN_ERR_SCALE = -6
 ATTN_ERR_LAUNCH = -7
 ATTN_ERR_ALIAS = -8
+ATTN_ERR_VARIANT = -9
+
+ATTN_VARIANT_AUTO = 0
+ATTN_VARIANT_PIPELINED = 1
+ATTN_VARIANT_PIPELINED_4STAGE = 2
+ATTN_VARIANT_SEQUENTIAL = 3
+ATTN_VARIANT_SPLIT = 4
+VARIANT_NAMES = {ATTN_VARIANT_AUTO: "auto", ATTN_VARIANT_PIPELINED: "pipelined",
+                 ATTN_VARIANT_PIPELINED_4STAGE: "pipelined_4stage", ATTN_VARIANT_SEQUENTIAL: "sequential",
+                 ATTN_VARIANT_SPLIT: "split"}
 
 
 class AttnError(RuntimeError):
@@ -57,6 +68,10 @@ def load_library(path=LIB_PATH):
     lib.attn_fwd.restype = ci
     lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, cf, cf, cf, vp]
     lib.attn_fwd_fp8.restype = ci
+    lib.attn_variant_available.argtypes = [ci, ci, ci]
+    lib.attn_variant_available.restype = ci
+    lib.attn_fwd_variant.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, cf, cf, cf, ci, vp]
+    lib.attn_fwd_variant.restype = ci
     lib.attn_quantize_fp8.argtypes = [vp, ci, vp, vp, ci, ci, ci, ci, ci, vp]
     lib.attn_quantize_fp8.restype = ci
     lib.attn_fwd_fp8_blockscaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
@@ -100,6 +115,20 @@ def attn_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, q_descale, k_d
                             float(v_descale), _stream(stream))
 
 
+def attn_variant_available(d, dtype, variant):
+    """The C ``attn_variant_available``: True if the variant is built for (d, dtype)."""
+    return bool(load_library().attn_variant_available(int(d), int(dtype), int(variant)))
+
+
+def attn_fwd_variant(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, q_descale, k_descale, v_descale,
+                     variant, stream=None):
+    """The C ``attn_fwd_variant``; returns its status code."""
+    lib = load_library()
+    return lib.attn_fwd_variant(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
+                                int(d), int(bool(causal)), float(scale), int(dtype), float(q_descale),
+                                float(k_descale), float(v_descale), int(variant), _stream(stream))
+
+
 def attn_quantize_fp8(x, dtype, codes, descales, B, H, N, d, hadamard, stream=None):
     """The C ``attn_quantize_fp8``; returns its status code."""
     lib = load_library()
@@ -131,13 +160,14 @@ def _dtype_code(t):
     raise TypeError(f"unsupported input dtype {t.dtype}")
 
 
-def attention(q, k, v, causal=False, scale=None, descale=None, stream=None):
+def attention(q, k, v, causal=False, scale=None, descale=None, stream=None, variant=None):
     """O, LSE for contiguous device tensors q [B,H,Nq,d], k, v [B,H,Nk,d].
 
     fp16 -> fp16 O, bf16 -> bf16 O, e4m3 (float8_e4m3fn or uint8 codes) ->
     fp16 O with ``descale = (q_descale, k_descale, v_descale)``.  LSE is
     float32 [B,H,Nq].  Runs on ``stream`` (default: current torch stream)
-    without synchronising.
+    without synchronising.  ``variant`` (an ATTN_VARIANT_* code) picks a
+    kernel variant through ``attn_fwd_variant``; None runs the default.
     """
     import torch
     B, H, Nq, d = q.shape
@@ -153,7 +183,10 @@ def attention(q, k, v, causal=False, scale=None, descale=None, stream=None):
     out_dtype = torch.bfloat16 if code == ATTN_BF16 else torch.float16
     o = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if code == ATTN_FP8_E4M3:
+    if variant is not None:
+        qd, kd, vd = descale if (descale is not None and code == ATTN_FP8_E4M3) else (1.0, 1.0, 1.0)
+        st = attn_fwd_variant(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, code, qd, kd, vd, variant, stream)
+    elif code == ATTN_FP8_E4M3:
         qd, kd, vd = descale if descale is not None else (1.0, 1.0, 1.0)
         st = attn_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, qd, kd, vd, stream)
     else:

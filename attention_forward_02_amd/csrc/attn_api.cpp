@@ -41,10 +41,29 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   return ATTN_OK;
 }
 
+bool variant_available(int d, int dtype, int variant) {
+  const bool d_ok = d == 64 || d == 128 || d == 256;
+  const bool t_ok = dtype == ATTN_F16 || dtype == ATTN_BF16 || dtype == ATTN_FP8_E4M3;
+  if (!d_ok || !t_ok) return false;
+  switch (variant) {
+    case ATTN_VARIANT_AUTO:
+    case ATTN_VARIANT_SEQUENTIAL:
+      return true;
+    case ATTN_VARIANT_PIPELINED:
+    case ATTN_VARIANT_PIPELINED_4STAGE:
+      return d != 256;
+    case ATTN_VARIANT_SPLIT:
+      return d == 64 && dtype != ATTN_FP8_E4M3;
+    default:
+      return false;
+  }
+}
+
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
-        int causal, float scale, int dtype, float q_ds, float k_ds, float v_ds, ihipStream_t* stream) {
+        int causal, float scale, int dtype, float q_ds, float k_ds, float v_ds, int variant, ihipStream_t* stream) {
   int st = validate(q, k, v, o, lse, B, H, Nq, Nk, d, dtype);
   if (st != ATTN_OK) return st;
+  if (!variant_available(d, dtype, variant)) return ATTN_ERR_VARIANT;
   if (!positive_finite(scale) || !positive_finite(q_ds) || !positive_finite(k_ds) || !positive_finite(v_ds))
     return ATTN_ERR_SCALE;
   const float s = scale * q_ds * k_ds;
@@ -65,6 +84,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   p.scale = s;
   p.v_descale = v_ds;
   p.q_descales = p.k_descales = p.v_descales = nullptr;
+  p.variant = variant;
   return attn::launch_forward(p, (hipStream_t)stream);
 }
 
@@ -74,13 +94,23 @@ extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
              int d, int causal, float scale, int dtype, ihipStream_t* stream) {
-  return run(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, 1.f, 1.f, 1.f, stream);
+  return run(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, 1.f, 1.f, 1.f, ATTN_VARIANT_AUTO, stream);
 }
 
 int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
                  int Nk, int d, int causal, float scale, float q_descale, float k_descale, float v_descale,
                  ihipStream_t* stream) {
   return run(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, ATTN_FP8_E4M3, q_descale, k_descale, v_descale,
+             ATTN_VARIANT_AUTO, stream);
+}
+
+int attn_variant_available(int d, int dtype, int variant) { return variant_available(d, dtype, variant) ? 1 : 0; }
+
+int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                     int d, int causal, float scale, int dtype, float q_descale, float k_descale, float v_descale,
+                     int variant, ihipStream_t* stream) {
+  if (dtype != ATTN_FP8_E4M3) q_descale = k_descale = v_descale = 1.f;
+  return run(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, q_descale, k_descale, v_descale, variant,
              stream);
 }
 
@@ -143,6 +173,7 @@ int attn_fwd_fp8_blockscaled(const void* q, const void* k, const void* v, const 
   p.q_descales = q_descales;
   p.k_descales = k_descales;
   p.v_descales = v_descales;
+  p.variant = ATTN_VARIANT_AUTO;
   return attn::launch_forward(p, (hipStream_t)stream);
 }
 
@@ -159,6 +190,7 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_SCALE: return "scale and descales must be finite and > 0";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
+    case ATTN_ERR_VARIANT: return "unknown kernel variant, or not built for this head dim and dtype";
     default: return "unknown status";
   }
 }

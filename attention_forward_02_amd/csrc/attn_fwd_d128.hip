@@ -11,6 +11,16 @@ template __global__ void attn_fwd_kernel<128, ATTN_F16, true>(Params);
 template __global__ void attn_fwd_kernel<128, ATTN_BF16, false>(Params);
 template __global__ void attn_fwd_kernel<128, ATTN_BF16, true>(Params);
 
+// Tuning variants (attn_fwd_variant).
+template __global__ void attn_fwd_kernel<128, ATTN_F16, false, 4>(Params);
+template __global__ void attn_fwd_kernel<128, ATTN_F16, true, 4>(Params);
+template __global__ void attn_fwd_kernel<128, ATTN_BF16, false, 4>(Params);
+template __global__ void attn_fwd_kernel<128, ATTN_BF16, true, 4>(Params);
+template __global__ void attn_fwd_seq_kernel<128, ATTN_F16, false>(Params);
+template __global__ void attn_fwd_seq_kernel<128, ATTN_F16, true>(Params);
+template __global__ void attn_fwd_seq_kernel<128, ATTN_BF16, false>(Params);
+template __global__ void attn_fwd_seq_kernel<128, ATTN_BF16, true>(Params);
+
 }  // namespace kernels
 
 int launch_forward_d128(const Problem& p, hipStream_t stream) { return kernels::launch_16bit<128>(p, stream); }

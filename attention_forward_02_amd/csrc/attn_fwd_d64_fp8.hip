@@ -12,6 +12,12 @@ template __global__ void attn_fwd_kernel<64, ATTN_FP8_E4M3, true>(Params);
 template __global__ void attn_fwd_seq_kernel<64, ATTN_FP8_E4M3, false, true>(Params);
 template __global__ void attn_fwd_seq_kernel<64, ATTN_FP8_E4M3, true, true>(Params);
 
+// Tuning variants (attn_fwd_variant).
+template __global__ void attn_fwd_kernel<64, ATTN_FP8_E4M3, false, 4>(Params);
+template __global__ void attn_fwd_kernel<64, ATTN_FP8_E4M3, true, 4>(Params);
+template __global__ void attn_fwd_seq_kernel<64, ATTN_FP8_E4M3, false>(Params);
+template __global__ void attn_fwd_seq_kernel<64, ATTN_FP8_E4M3, true>(Params);
+
 }  // namespace kernels
 
 int launch_forward_d64_fp8(const Problem& p, hipStream_t stream) { return kernels::launch_fp8<64>(p, stream); }

@@ -497,6 +497,31 @@ __device__ __forceinline__ i16x8 pack8(const f32x16& p, int base) {
                                          pack16<DT>(p[base + 4], p[base + 5]), pack16<DT>(p[base + 6], p[base + 7])});
 }
 
+// Row sum (this lane's half) of packed binary16 P, NP 8-element fragments,
+// with v_dot2_f32_f16 against (1, 1): half the instructions of fp32 adds.
+// It sums P as rounded for the MFMA (relative error below 2^-11 per term, so
+// |dLSE| stays below 5e-4 in the worst case), which also makes the
+// normalisation consistent with the P V product.  bfloat16's coarser
+// rounding could move LSE by up to 2e-3, so bf16 keeps the fp32 sum of the
+// unrounded p.
+template <int NP>
+__device__ __forceinline__ float row_sum_f16(const i16x8 (&pf)[4]) {
+  float l[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const u32x4 w = __builtin_bit_cast(u32x4, pf[i]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // Copy the element out first: a bit cast applied directly to a vector
+      // element reads element 0.
+      const uint32_t we = w[e];
+      l[e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, we), (f16x2){(_Float16)1.0f, (_Float16)1.0f}, l[e],
+                                    false);
+    }
+  }
+  return (l[0] + l[1]) + (l[2] + l[3]);
+}
+
 // P^T as the E4M3 B operand of the P V MFMA: byte 16s + r holds element r
 // of the tile's s-th score accumulator.
 __device__ __forceinline__ i32x8 pack_p_fp8(const f32x16& p0, const f32x16& p1) {
@@ -654,28 +679,7 @@ __device__ __forceinline__ void step(WaveState<D, DT>& st, const LoopCtx& cx, in
     ATTN_INTERLEAVE(3, D / 8, kValuA, 1);
     // Phase B
     pv_tile<D, DT>(st, pf, Vs);
-    if constexpr (DT == ATTN_F16) {
-      // Row sum from the packed binary16 P with v_dot2_f32_f16 against
-      // (1, 1): half the instructions of fp32 adds.  It sums P as rounded
-      // for the MFMA (relative error below 2^-11 per term, so |dLSE| stays
-      // below 5e-4 in the worst case), which also makes the normalisation
-      // consistent with the P V product.  bfloat16's coarser rounding could
-      // move LSE by up to 2e-3, so bf16 keeps the fp32 sum of unrounded p.
-      float l[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 w = __builtin_bit_cast(u32x4, pf[i]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // Copy the element out first: a bit cast applied directly to a
-          // vector element reads element 0.
-          const uint32_t we = w[e];
-          l[e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, we), (f16x2){(_Float16)1.0f, (_Float16)1.0f}, l[e],
-                                        false);
-        }
-      }
-      st.lrun += (l[0] + l[1]) + (l[2] + l[3]);
-    }
+    if constexpr (DT == ATTN_F16) st.lrun += row_sum_f16<4>(pf);
   }
   if constexpr (DT != ATTN_F16) {
     float ls0 = 0.f, ls1 = 0.f;
@@ -757,26 +761,40 @@ struct Waves {
   static constexpr int value = D == 128 ? 8 : 4;
 };
 
-template <int D, int DT, bool CAUSAL>
+// NS: stages of the K ring and of the V ring, 2 (the default) or 4.  With
+// four, the workgroup synchronises once per two key tiles instead of once
+// per tile and loads run a whole step pair ahead, for twice the LDS; on
+// 16-bit d = 128 that measured 1.5% slower, so it is a tuning variant.
+template <int D, int DT, bool CAUSAL, int NS = 2>
 __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_kernel(Params p) {
+  static_assert(NS == 2 || NS == 4, "two or four ring stages");
   constexpr int kWaves = Waves<D, DT>::value;
   constexpr int kBlockM = kWaves * kRowsPerWave;  // query rows per workgroup
   constexpr int kRowBytes = D * Fmt<DT>::kBytes;
   constexpr int kTileBytes = kBlockN * kRowBytes;
-  // K and V rings of two stages each, as four separate LDS objects.  K runs
-  // one tile ahead of V: step j reads K_{j+1} (scores of the next tile) and
-  // V_j while K_{j+2} and V_{j+1} stream in.  With every stage a distinct
-  // object and the loop unrolled by two, each LDS read names its stage
-  // statically, so the compiler can prove it never aliases the in-flight
-  // direct-to-LDS loads into another stage and does not wait on them.
+  constexpr int kExtraBytes = NS == 4 ? kTileBytes : 16;
+  // K and V rings of NS stages each, as separate LDS objects.  K runs one
+  // tile ahead of V: step j reads K_{j+1} (scores of the next tile) and V_j.
+  // With every stage a distinct object and the loop unrolled over a whole
+  // turn of the ring, each LDS read names its stage statically, so the
+  // compiler can prove it never aliases the in-flight direct-to-LDS loads
+  // into another stage and does not wait on them.
   __shared__ __attribute__((aligned(1024))) unsigned char k_st0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char k_st1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char v_st0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char v_st1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st2[kExtraBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st3[kExtraBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st2[kExtraBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st3[kExtraBytes];
   lds_t* const K0 = (lds_t*)k_st0;
   lds_t* const K1 = (lds_t*)k_st1;
   lds_t* const V0 = (lds_t*)v_st0;
   lds_t* const V1 = (lds_t*)v_st1;
+  lds_t* const K2 = (lds_t*)k_st2;
+  lds_t* const K3 = (lds_t*)k_st3;
+  lds_t* const V2 = (lds_t*)v_st2;
+  lds_t* const V3 = (lds_t*)v_st3;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -809,12 +827,69 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_kernel(Pa
   // Scores (then probabilities) of even tiles live in (a0, a1), of odd
   // tiles in (b0, b1).
   f32x16 a0, a1, b0, b1;
-  // Tiles before tb need no mask bias; step j works on the scores of tile
-  // j + 1, so steps j < jm (jm even, so the second loop again starts with
-  // S_j in (a0, a1)) run the unmasked step and the rest the masked one.  Two
-  // loops with one step variant each keep the register assignment of the
-  // unrolled pair identical on every iteration.
   const int tb = first_bias_tile<CAUSAL>(cx);
+  if constexpr (NS == 4) {
+    // Tile t sits in stage t % 4 of each ring.  Steps run in pairs (j, j+1),
+    // j even, behind one barrier: the pair reads K_{j+1}, K_{j+2}, V_j,
+    // V_{j+1}, while K_{j+3}, K_{j+4}, V_{j+2}, V_{j+3} stream into the
+    // stages the previous pair read.  Every K stage a step reads holds
+    // finite data: the stages start with tiles 0..2 (and tile 3 when the
+    // loop does not load it), rows past the end arriving as zeros through
+    // the range check; later a stage past the last tile keeps an earlier
+    // tile.  Scores of tiles past the end are masked to -inf.
+    if (nt > 0) {
+      ld.load(K0, Kr, 0);
+      ld.load(V0, Vr, 0);
+      ld.load(K1, Kr, kBlockN);
+      ld.load(V1, Vr, kBlockN);
+      ld.load(K2, Kr, 2 * kBlockN);
+      if (nt <= 3) ld.load(K3, Kr, 3 * kBlockN);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tb > 0) masked_scores<D, DT, CAUSAL, false>(st, cx, 0, K0, a0, a1);
+      else masked_scores<D, DT, CAUSAL, true>(st, cx, 0, K0, a0, a1);
+      bool rescale;
+      update_reference(st.m2, tile_max2(a0, a1, cx.c), rescale);
+    }
+    // Four steps from j (j % 4 == 0); returns false after the last step.
+    auto four_steps = [&](int j, auto masked) -> bool {
+      constexpr bool M = decltype(masked)::value;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (j + 3 < nt) ld.load(K3, Kr, (j + 3) * kBlockN);
+      if (j + 4 < nt) ld.load(K0, Kr, (j + 4) * kBlockN);
+      if (j + 2 < nt) ld.load(V2, Vr, (j + 2) * kBlockN);
+      if (j + 3 < nt) ld.load(V3, Vr, (j + 3) * kBlockN);
+      step<D, DT, CAUSAL, M>(st, cx, j, a0, a1, b0, b1, K1, V0);
+      if (j + 1 >= nt) return false;
+      step<D, DT, CAUSAL, M>(st, cx, j + 1, b0, b1, a0, a1, K2, V1);
+      if (j + 2 >= nt) return false;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (j + 5 < nt) ld.load(K1, Kr, (j + 5) * kBlockN);
+      if (j + 6 < nt) ld.load(K2, Kr, (j + 6) * kBlockN);
+      if (j + 4 < nt) ld.load(V0, Vr, (j + 4) * kBlockN);
+      if (j + 5 < nt) ld.load(V1, Vr, (j + 5) * kBlockN);
+      step<D, DT, CAUSAL, M>(st, cx, j + 2, a0, a1, b0, b1, K3, V2);
+      if (j + 3 >= nt) return false;
+      step<D, DT, CAUSAL, M>(st, cx, j + 3, b0, b1, a0, a1, K0, V3);
+      return j + 4 < nt;
+    };
+    // Steps j < jm (a multiple of 4) need no mask bias for the tile they
+    // score (j + 1 < tb); the rest run the masked variant.
+    const int jm = tb > 1 ? (tb - 1) & ~3 : 0;
+    int j = 0;
+    for (; j < jm; j += 4) four_steps(j, BoolTag<false>{});
+    for (; j < nt; j += 4)
+      if (!four_steps(j, BoolTag<true>{})) break;
+    store_output<D, DT>(p, st, bh, cx.qrow, cx.half);
+    return;
+  }
+  // Two stages.  Tiles before tb need no mask bias; step j works on the
+  // scores of tile j + 1, so steps j < jm (jm even, so the second loop again
+  // starts with S_j in (a0, a1)) run the unmasked step and the rest the
+  // masked one.  Two loops with one step variant each keep the register
+  // assignment of the unrolled pair identical on every iteration.
   const int jm = tb > 1 ? (tb - 1) & ~1 : 0;
   if (nt > 0) {
     // K_1 is loaded even when there is no tile 1: its rows then fail the
@@ -899,6 +974,10 @@ __device__ __forceinline__ void seq_step(WaveState<D, DT>& st, const LoopCtxT<BN
       pf[3] = pack8<DT>(s1, 8);
     }
     pv_tile<D, DT, BN>(st, pf, Vc);
+    if constexpr (DT == ATTN_F16) {
+      st.lrun += row_sum_f16<BN / 16>(pf);
+      return;
+    }
   }
   float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
@@ -1173,6 +1252,17 @@ struct Sequential {
   static constexpr bool value = (D == 128 && DT == ATTN_FP8_E4M3) || D == 256;
 };
 
+// Kernel choices a caller can make (include/attn.h, attn_fwd_variant):
+// the pipelined kernel with a two- or four-stage ring (not at d = 256, whose
+// pipelined registers leave one wave per SIMD), the sequential kernel, and
+// the split-key kernel (16-bit d = 64).  ATTN_VARIANT_AUTO takes the
+// measured defaults above.
+template <int D, int DT>
+struct Variants {
+  static constexpr bool pipelined = D != 256;
+  static constexpr bool split = UseSplit<D, DT>::value;
+};
+
 // ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
@@ -1196,22 +1286,45 @@ int launch_one(const Problem& pr, hipStream_t stream) {
   p.o_scale = pr.v_descale;
   p.qs = p.ks = p.vs = nullptr;
   p.nqb = p.nkb = 0;
-  if constexpr (UseSplit<D, DT>::value) {
+  const int n128 = (pr.Nq + 127) / 128;
+  const long long grid128 = (long long)pr.B * pr.H * n128;
+  int variant = pr.variant;
+  if (variant == ATTN_VARIANT_AUTO) {
+    variant = Sequential<D, DT>::value ? ATTN_VARIANT_SEQUENTIAL : ATTN_VARIANT_PIPELINED;
     // Split-key kernel while 128-row query tiles do not fill two rounds of
     // the 256 CUs (and there are enough of them to be worth splitting).
-    const int n128 = (pr.Nq + 127) / 128;
-    const long long grid = (long long)pr.B * pr.H * n128;
-    if (grid >= kSplitMinGrid && grid <= kSplitMaxGrid) {
-      p.n_qtiles = n128;
-      p.total_tiles = (int)grid;
-      hipLaunchKernelGGL((attn_fwd_split_kernel<D, DT, CAUSAL>), dim3(p.total_tiles), dim3(512), 0, stream, p);
-      return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
-    }
+    if (UseSplit<D, DT>::value && grid128 >= kSplitMinGrid && grid128 <= kSplitMaxGrid)
+      variant = ATTN_VARIANT_SPLIT;
   }
-  if constexpr (Sequential<D, DT>::value)
-    hipLaunchKernelGGL((attn_fwd_seq_kernel<D, DT, CAUSAL>), dim3(p.total_tiles), dim3(64 * kWaves), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL>), dim3(p.total_tiles), dim3(64 * kWaves), 0, stream, p);
+  const dim3 block(64 * kWaves);
+  switch (variant) {
+    case ATTN_VARIANT_SPLIT:
+      if constexpr (Variants<D, DT>::split) {
+        if (grid128 > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+        p.n_qtiles = n128;
+        p.total_tiles = (int)grid128;
+        hipLaunchKernelGGL((attn_fwd_split_kernel<D, DT, CAUSAL>), dim3(p.total_tiles), dim3(512), 0, stream, p);
+        break;
+      }
+      return ATTN_ERR_VARIANT;
+    case ATTN_VARIANT_SEQUENTIAL:
+      hipLaunchKernelGGL((attn_fwd_seq_kernel<D, DT, CAUSAL>), dim3(p.total_tiles), block, 0, stream, p);
+      break;
+    case ATTN_VARIANT_PIPELINED:
+      if constexpr (Variants<D, DT>::pipelined) {
+        hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL, 2>), dim3(p.total_tiles), block, 0, stream, p);
+        break;
+      }
+      return ATTN_ERR_VARIANT;
+    case ATTN_VARIANT_PIPELINED_4STAGE:
+      if constexpr (Variants<D, DT>::pipelined) {
+        hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL, 4>), dim3(p.total_tiles), block, 0, stream, p);
+        break;
+      }
+      return ATTN_ERR_VARIANT;
+    default:
+      return ATTN_ERR_VARIANT;
+  }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

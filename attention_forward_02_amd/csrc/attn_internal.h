@@ -24,6 +24,7 @@ struct Problem {
   const float* q_descales;
   const float* k_descales;
   const float* v_descales;
+  int variant;        // ATTN_VARIANT_*; AUTO for attn_fwd / attn_fwd_fp8
 };
 
 // Launches the forward pass on `stream`.  Returns 0 or a negative ATTN_ERR_*.

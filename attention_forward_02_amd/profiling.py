@@ -217,7 +217,9 @@ def summarize(outdir, workload):
     lines.append("")
     os.makedirs(PROFILES, exist_ok=True)
     md = os.path.join(PROFILES, f"{kname}_{workload}.md")
-    for old in glob.glob(os.path.join(PROFILES, f"*_{workload}.md")):
+    # an earlier summary of the same workload under another kernel name (not
+    # the tuning tables, profiles/tuning_<workload>.md)
+    for old in glob.glob(os.path.join(PROFILES, f"attn_*_{workload}.md")):
         if old != md:
             os.remove(old)
     with open(md, "w") as f:

@@ -76,7 +76,28 @@ enum {
                              not 4-byte aligned */
   ATTN_ERR_SCALE = -6,    /* scale or a descale is not finite and > 0 */
   ATTN_ERR_LAUNCH = -7,   /* the kernel launch failed */
-  ATTN_ERR_ALIAS = -8     /* an output overlaps an input or another output */
+  ATTN_ERR_ALIAS = -8,    /* an output overlaps an input or another output */
+  ATTN_ERR_VARIANT = -9   /* unknown kernel variant, or not built for this d and dtype */
+};
+
+/* Kernel variants (attn_fwd_variant).  All compute the same result; they
+ * differ in schedule, so their speed depends on the shape:
+ *   AUTO               the library's measured default for the (d, dtype,
+ *                      shape) -- what attn_fwd and attn_fwd_fp8 run
+ *   PIPELINED          scores of the next key tile computed under the
+ *                      softmax of the current one, 2-stage K/V ring
+ *                      (d = 64, 128)
+ *   PIPELINED_4STAGE   the same with a 4-stage ring and one workgroup
+ *                      barrier per two key tiles (d = 64, 128)
+ *   SEQUENTIAL         one key tile per step, no score pipelining (all d)
+ *   SPLIT              two wave groups over the two halves of the key range,
+ *                      merged at the end (16-bit d = 64) */
+enum {
+  ATTN_VARIANT_AUTO = 0,
+  ATTN_VARIANT_PIPELINED = 1,
+  ATTN_VARIANT_PIPELINED_4STAGE = 2,
+  ATTN_VARIANT_SEQUENTIAL = 3,
+  ATTN_VARIANT_SPLIT = 4
 };
 
 /*
@@ -110,6 +131,25 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int H, int Nq, int Nk, int d, int causal, float scale,
                  float q_descale, float k_descale, float v_descale,
                  struct ihipStream_t* stream);
+
+/*
+ * attn_variant_available: 1 if `variant` is built for head dimension d and
+ * `dtype` (an attn_dtype), else 0.  Host-only; touches no device.
+ */
+int attn_variant_available(int d, int dtype, int variant);
+
+/*
+ * attn_fwd_variant: attn_fwd / attn_fwd_fp8 with an explicit kernel
+ * variant, for measuring which one suits a shape (tile and stage tuning).
+ * Arguments as attn_fwd_fp8 (the descales are used only for ATTN_FP8_E4M3;
+ * pass 1 otherwise), plus `variant` (an ATTN_VARIANT_* code).  Returns
+ * ATTN_ERR_VARIANT, before touching the device, for a variant that
+ * attn_variant_available rejects.
+ */
+int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                     int dtype, float q_descale, float k_descale, float v_descale,
+                     int variant, struct ihipStream_t* stream);
 
 /*
  * attn_quantize_fp8: block-scaled FP8 E4M3 quantisation of one attention

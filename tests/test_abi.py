@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     assert set(_declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_fwd_fp8_blockscaled",
-                                          "attn_status_str"}
+                                          "attn_variant_available", "attn_fwd_variant", "attn_status_str"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -140,6 +140,44 @@ def test_blockscaled_validation_rejects_before_launch(kw, code):
     a.update(kw)
     st = _lib().attn_fwd_fp8_blockscaled(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"],
                                          a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], None)
+    assert st == code
+
+
+def test_variant_codes_match_header():
+    src = open(HEADER).read()
+    codes = dict((k, int(v)) for k, v in re.findall(r"(ATTN_VARIANT_\w+)\s*=\s*(\d+)", src))
+    assert codes == {"ATTN_VARIANT_AUTO": 0, "ATTN_VARIANT_PIPELINED": 1, "ATTN_VARIANT_PIPELINED_4STAGE": 2,
+                     "ATTN_VARIANT_SEQUENTIAL": 3, "ATTN_VARIANT_SPLIT": 4}
+    for name, val in codes.items():
+        assert getattr(b, name) == val
+
+
+def test_variant_availability_table():
+    lib = _lib()
+    for d in (64, 128, 256):
+        for dt in (b.ATTN_F16, b.ATTN_BF16, b.ATTN_FP8_E4M3):
+            got = {v for v in range(-1, 7) if lib.attn_variant_available(d, dt, v)}
+            want = {b.ATTN_VARIANT_AUTO, b.ATTN_VARIANT_SEQUENTIAL}
+            if d != 256:
+                want |= {b.ATTN_VARIANT_PIPELINED, b.ATTN_VARIANT_PIPELINED_4STAGE}
+            if d == 64 and dt != b.ATTN_FP8_E4M3:
+                want.add(b.ATTN_VARIANT_SPLIT)
+            assert got == want, (d, dt, got)
+    assert not lib.attn_variant_available(96, b.ATTN_F16, 0) and not lib.attn_variant_available(64, 5, 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(variant=5), b.ATTN_ERR_VARIANT), (dict(variant=-1), b.ATTN_ERR_VARIANT),
+    (dict(d=256, variant=1), b.ATTN_ERR_VARIANT), (dict(d=256, variant=2), b.ATTN_ERR_VARIANT),
+    (dict(dtype=2, variant=4), b.ATTN_ERR_VARIANT), (dict(d=128, variant=4), b.ATTN_ERR_VARIANT),
+    (dict(q=None, variant=1), b.ATTN_ERR_NULL), (dict(d=80, variant=1), b.ATTN_ERR_HEADDIM),
+    (dict(dtype=2, kd=0.0), b.ATTN_ERR_SCALE), (dict(lse=O + 64), b.ATTN_ERR_ALIAS),
+])
+def test_variant_validation_rejects_before_launch(kw, code):
+    a = dict(GOOD, qd=1.0, kd=1.0, vd=1.0, variant=1)
+    a.update(kw)
+    st = _lib().attn_fwd_variant(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                                 a["causal"], a["scale"], a["dtype"], a["qd"], a["kd"], a["vd"], a["variant"], None)
     assert st == code
 
 

@@ -41,6 +41,9 @@
 //     tile, for a step bound by softmax VALU work or by registers;
 //   * attn_fwd_split_kernel (16-bit d = 64, mid-size grids): two wave groups
 //     walk the two halves of the key range and merge.
+// Those are the defaults (launch_one).  Every kernel built for a (d,
+// format) can also be requested explicitly as a tuning variant, including
+// the pipelined kernel with a four-stage K/V ring.
 // Masking is folded into the initial values of the score accumulators; the
 // key loops run the unmasked steps and the masked ones (ragged end, causal
 // diagonal) as two loops of one step variant each, so every step is one

@@ -171,3 +171,22 @@ def test_smoothing_lowers_error_on_outliers():
     say(f"[gpu] relative RMSE against the float32 inputs: per-tensor {r_pt:.4g}, smoothed block-scaled {r_sm:.4g} "
         f"({r_pt / r_sm:.2f}x lower)")
     assert r_sm < r_pt / 1.2
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_smoothed_path_end_to_end_causal(d, dtype):
+    # quantiser and forward chained on the GPU, causal, Nq != Nk, ragged
+    label = f"smoothed end to end d={d} {dtype} causal Nq=333 Nk=400"
+    say(f"[gpu] {label}: B=1 H=2")
+    inp = inputs.make(1, 2, 333, 400, d, dtype, seed=d + 5, outliers=True)
+    q, k, v = (upload(t, dtype) for t in (inp.q, inp.k, inp.v))
+    o, lse = attention_fp8_smoothed(q, k, v, causal=True, scale=float(inp.scale))
+    torch.cuda.synchronize()
+    x = [decode(t, dtype) for t in (inp.q, inp.k, inp.v)]
+    deq = [oracle.dequantize_blocks(*oracle.quantize_blocks(t, had)) for t, had in zip(x, (True, True, False))]
+    o_ref, lse_ref = oracle.attention(*deq, True, float(inp.scale))
+    o_codes = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    stats = compare(o_codes, lse.cpu().numpy(), o_ref, lse_ref, "e4m3", label,
+                    lse_tol=fp8_lse_tol(deq[0], deq[1], float(inp.scale)))
+    say(f"[gpu] {label}: {stats}")

@@ -13,9 +13,16 @@
 //   2. the block's largest magnitude comes from a wave reduction plus one
 //      LDS exchange between the four waves; descale = amax / 448 in IEEE
 //      float32 (1 for an all-zero block);
-//   3. every value is divided by the descale (IEEE float32 division) and
-//      rounded to E4M3 by v_cvt_pk_fp8_f32 (round to nearest even); each
-//      group leaves as one 16-byte store.
+//   3. every value is divided by the descale and rounded to E4M3 by
+//      v_cvt_pk_fp8_f32 (round to nearest even); each group leaves as one
+//      16-byte store.  The quotient is the IEEE float32 one, RN(y / ds),
+//      from a multiply and two FMAs per value: with r = RN(1 / ds) (one
+//      correctly rounded division per thread), q = RN(y r) is within one ulp
+//      of y / ds, the residual y - ds q is exact in an FMA, and q + (y - ds q) r
+//      rounds to RN(y / ds) (Markstein's theorem on FMA division).  The
+//      theorem needs the residual to stay a normal number wherever it can
+//      move a code, which holds for ds >= 2^-90; smaller descales (bfloat16
+//      blocks of magnitude below about 1e-25) take the plain division.
 // The block stays in registers between the passes, so every input byte is
 // read once and every code written once.
 #include <hip/hip_runtime.h>
@@ -114,20 +121,33 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(const uint16_t* __re
   const float ds = amax > 0.f ? amax / kE4m3Max : 1.f;
   if (threadIdx.x == 0) descales[blockIdx.x] = ds;
 
+  auto emit = [&](auto quot) {
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int g = threadIdx.x + i * kThreads;
-    const int r = r0 + g / kGroups;
-    if (r < N) {
-      u32x4 out;
+    for (int i = 0; i < kPer; ++i) {
+      const int g = threadIdx.x + i * kThreads;
+      const int r = r0 + g / kGroups;
+      if (r < N) {
+        u32x4 out;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float* p = &y[i][4 * w];
-        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] / ds, p[1] / ds, 0, false);
-        out[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[2] / ds, p[3] / ds, lo, true);
+        for (int w = 0; w < 4; ++w) {
+          const float* p = &y[i][4 * w];
+          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(quot(p[0]), quot(p[1]), 0, false);
+          out[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quot(p[2]), quot(p[3]), lo, true);
+        }
+        *(u32x4*)(codes + (head + r) * D + (g % kGroups) * 16) = out;
       }
-      *(u32x4*)(codes + (head + r) * D + (g % kGroups) * 16) = out;
     }
+  };
+  if (ds >= 0x1p-90f) {  // block-uniform
+    const float rcp = 1.f / ds;
+    emit([&](float v) {
+      // The residual is formed as ds q - v and subtracted, so that v = -0
+      // gives -0 (as v / ds does) rather than +0 + -0 = +0.
+      const float q = v * rcp;
+      return __builtin_fmaf(-__builtin_fmaf(ds, q, -v), rcp, q);
+    });
+  } else {
+    emit([&](float v) { return v / ds; });
   }
 }
 

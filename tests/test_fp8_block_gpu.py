@@ -73,6 +73,22 @@ def test_quantize_zero_and_small_blocks():
             _assert_quant_equal(enc(x), dtype, had, f"special blocks {dtype} hadamard={had}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_quantize_block_magnitudes(dtype):
+    # every 64-row block at its own magnitude: bfloat16 down to 1e-36 (the
+    # quantiser's plain-division path below descale 2^-90) and up to 1e30,
+    # binary16 across its normal range
+    say(f"[gpu] quantize: block magnitudes {dtype}")
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((1, 2, 64 * 12, 128)).astype(np.float32)
+    lo, hi = (-120, 100) if dtype == "bf16" else (-12, 12)
+    for b in range(12):
+        x[:, :, 64 * b:64 * (b + 1)] *= np.float32(2.0 ** rng.integers(lo, hi))
+    enc = inputs.encode_bf16 if dtype == "bf16" else inputs.encode_f16
+    for had in (False, True):
+        _assert_quant_equal(enc(x), dtype, had, f"block magnitudes {dtype} hadamard={had}")
+
+
 def _blockscaled_case(B, H, nq, nk, d, causal, seed):
     """Oracle codes and descales (Q, K smoothed), uploaded; returns GPU
     (O codes, LSE) and the oracle's (O, LSE) plus the dequantised q, k."""

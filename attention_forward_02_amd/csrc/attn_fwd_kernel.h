@@ -753,15 +753,14 @@ struct TileKeys {
   static constexpr int value = (D == 256 && DT != ATTN_FP8_E4M3) ? 32 : 64;
 };
 
-// Waves per workgroup (32 query rows each).  At d = 128 one 8-wave
+// Waves per workgroup (32 query rows each).  At d = 128 and 256 one 8-wave
 // workgroup per CU (two waves per SIMD, 256 query rows) shares each K/V
 // tile among twice the rows of two 4-wave workgroups, halving the
-// global-to-LDS loads per FLOP; measured faster there.  Elsewhere 4 waves:
-// d = 64 measured slower with 8, and d = 256 needs one workgroup's whole LDS
-// share for its 4 waves.
+// global-to-LDS loads per FLOP: measured +0.9% at d = 128 and +1.5% at
+// d = 256 (causal bf16).  At d = 64, 4 waves measured faster.
 template <int D, int DT>
 struct Waves {
-  static constexpr int value = D == 128 ? 8 : 4;
+  static constexpr int value = (D == 128 || D == 256) ? 8 : 4;
 };
 
 // NS: stages of the K ring and of the V ring, 2 (the default) or 4.  With

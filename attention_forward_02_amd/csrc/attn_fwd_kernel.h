@@ -602,7 +602,7 @@ struct BoolTag {
 };
 
 // Scores of tile t (K from Ks) into (s0, s1).  MASKED: the accumulators
-// start from the tile's mask bias (see score_bias); else from zero.
+// start from the tile's mask bias (see needs_bias); else from zero.
 template <int D, int DT, bool CAUSAL, bool MASKED, int BN>
 __device__ __forceinline__ void masked_scores(const WaveState<D, DT>& st, const LoopCtxT<BN>& cx, int t,
                                               const lds_t* Ks, f32x16& s0, f32x16& s1) {

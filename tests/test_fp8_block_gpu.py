@@ -206,3 +206,39 @@ def test_smoothed_path_end_to_end_causal(d, dtype):
     stats = compare(o_codes, lse.cpu().numpy(), o_ref, lse_ref, "e4m3", label,
                     lse_tol=fp8_lse_tol(deq[0], deq[1], float(inp.scale)))
     say(f"[gpu] {label}: {stats}")
+
+
+def test_canaries_and_side_stream():
+    # quantiser and block-scaled forward on a non-default stream: nothing is
+    # written past the ends of codes, descales, o and lse, every element is
+    # written, and the results equal those on the default stream bitwise
+    from attention_forward_02_amd import attn_fwd_fp8_blockscaled, attn_quantize_fp8
+    from attention_forward_02_amd.binding import ATTN_F16, ATTN_OK
+    B, H, N, d = 1, 3, 333, 128
+    nb = (N + 63) // 64
+    inp = inputs.make(B, H, N, N, d, "f16", seed=23, outliers=True)
+    q, k, v = (upload(t, "f16") for t in (inp.q, inp.k, inp.v))
+    n, pad = B * H * N * d, 4096
+    results = []
+    for use_stream in (False, True):
+        say(f"[gpu] block-scaled canary run, non-default stream={use_stream}")
+        stream = torch.cuda.Stream() if use_stream else torch.cuda.current_stream()
+        codes = [torch.full((n + pad,), 0xA5, dtype=torch.uint8, device="cuda") for _ in range(3)]
+        ds = [torch.full((B * H * nb + 64,), -7.0, dtype=torch.float32, device="cuda") for _ in range(3)]
+        o = torch.full((n + pad,), 1234.0, dtype=torch.float16, device="cuda")
+        lse = torch.full((B * H * N + 64,), 4321.0, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for t, c, s_, had in zip((q, k, v), codes, ds, (True, True, False)):
+                assert attn_quantize_fp8(t, ATTN_F16, c, s_, B, H, N, d, had, stream) == ATTN_OK
+            st = attn_fwd_fp8_blockscaled(*codes, *ds, o, lse, B, H, N, N, d, True, float(inp.scale), stream)
+            assert st == ATTN_OK
+        stream.synchronize()
+        for c, s_ in zip(codes, ds):
+            assert torch.all(c[n:] == 0xA5) and torch.all(s_[B * H * nb:] == -7.0), "write past the end"
+            assert torch.all(s_[:B * H * nb] > 0), "a descale was not written"
+        assert torch.all(o[n:] == 1234.0) and torch.all(lse[B * H * N:] == 4321.0), "write past the end of o / lse"
+        assert not torch.any(lse[:B * H * N] == 4321.0), "an LSE element was not written"
+        results.append([x.clone() for x in (*codes, *ds, o, lse)])
+    for a, b in zip(*results):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "default and side stream differ"

@@ -41,9 +41,10 @@ ATTN_VARIANT_PIPELINED = 1
 ATTN_VARIANT_PIPELINED_4STAGE = 2
 ATTN_VARIANT_SEQUENTIAL = 3
 ATTN_VARIANT_SPLIT = 4
+ATTN_VARIANT_PINGPONG = 5
 VARIANT_NAMES = {ATTN_VARIANT_AUTO: "auto", ATTN_VARIANT_PIPELINED: "pipelined",
                  ATTN_VARIANT_PIPELINED_4STAGE: "pipelined_4stage", ATTN_VARIANT_SEQUENTIAL: "sequential",
-                 ATTN_VARIANT_SPLIT: "split"}
+                 ATTN_VARIANT_SPLIT: "split", ATTN_VARIANT_PINGPONG: "pingpong"}
 
 
 class AttnError(RuntimeError):

@@ -933,6 +933,195 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_kernel(Pa
 }
 
 // ---------------------------------------------------------------------------
+// Pingpong kernel (16-bit, d = 128): the pages' two-consumer schedule
+// (concept card, "Pingpong scheduling between two consumer warpgroups";
+// "Inside FlashAttention-3", section 3).  The workgroup's 8 waves form two
+// groups, A = waves 0-3 and B = waves 4-7, so every SIMD holds one wave of
+// each.  Every wave alternates
+//   * an MFMA half: O += P_j V_j and S_{j+1} = K_{j+1} Q^T, with nothing but
+//     their LDS operand reads beside them, at s_setprio 1, and
+//   * a softmax half: S_{j+1} -> P_{j+1} (row max and reference update, exp2,
+//     rounding, row sum), with no matrix work;
+// group B runs one half behind group A and every half ends at a workgroup
+// barrier, so on each SIMD one wave's matrix work overlaps the other wave's
+// softmax.  The softmax half consumes the score tile before the next MFMA
+// half overwrites it, so a wave holds one score tile (fewer registers than
+// the pipelined kernel's two).
+//
+// Ring: K and V in two stages each.  K_{j+2} and V_{j+1} are loaded at the
+// start of A's MFMA half j (= B's softmax half j) into the stages both
+// groups finished reading one half earlier; A waits for its share at the end
+// of its next softmax half, B at the end of its MFMA half j.
+// ---------------------------------------------------------------------------
+template <int D, int DT, bool CAUSAL, bool MASKED, bool PV>
+__device__ __forceinline__ void pp_mfma_half(WaveState16<D, DT>& st, const LoopCtx& cx, int j, const i16x8 (&pf)[4],
+                                             f32x16& s0, f32x16& s1, const lds_t* Kn, const lds_t* Vc) {
+  __builtin_amdgcn_s_setprio(1);
+  masked_scores<D, DT, CAUSAL, MASKED>(st, cx, j + 1, Kn, s0, s1);
+  if constexpr (PV) pv_tile<D, DT>(st, pf, Vc);
+  // scores: 3 K reads ahead, one per MFMA; P V: 4 V reads ahead, two per MFMA
+  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+  for (int i = 0; i < 2 * D / 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  if constexpr (PV) {
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+}
+
+template <int D, int DT>
+__device__ __forceinline__ void pp_softmax_half(WaveState16<D, DT>& st, const LoopCtx& cx, f32x16& s0, f32x16& s1,
+                                                i16x8 (&pf)[4]) {
+  bool rescale;
+  const float alpha = update_reference(st.m2, tile_max2(s0, s1, cx.c), rescale);
+  if (rescale) {
+    asm volatile("" ::: "memory");  // keep the branch (see step)
+    st.lrun *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha;
+  }
+  const float mref = (st.m2 == -__builtin_inff()) ? 0.f : st.m2;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cx.c, -mref));
+    s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cx.c, -mref));
+  }
+  pf[0] = pack8<DT>(s0, 0);
+  pf[1] = pack8<DT>(s0, 8);
+  pf[2] = pack8<DT>(s1, 0);
+  pf[3] = pack8<DT>(s1, 8);
+  if constexpr (DT == ATTN_F16) {
+    st.lrun += row_sum_f16<4>(pf);
+  } else {
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      ls0 += s0[r];
+      ls1 += s1[r];
+    }
+    st.lrun += ls0 + ls1;
+  }
+}
+
+template <int D, int DT, bool CAUSAL>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) attn_fwd_pingpong_kernel(Params p) {
+  static_assert(D == 128 && DT != ATTN_FP8_E4M3, "pingpong kernel: 16-bit, d = 128");
+  constexpr int kWaves = 8;
+  constexpr int kBlockM = kWaves * kRowsPerWave;
+  constexpr int kRowBytes = D * 2;
+  constexpr int kTileBytes = kBlockN * kRowBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st1[kTileBytes];
+  lds_t* const K0 = (lds_t*)k_st0;
+  lds_t* const K1 = (lds_t*)k_st1;
+  lds_t* const V0 = (lds_t*)v_st0;
+  lds_t* const V1 = (lds_t*)v_st1;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2;  // 0: group A, 1: group B (one half behind)
+
+  int bh, qt;
+  schedule(p, blockIdx.x, CAUSAL, bh, qt);
+  const int q0 = qt * kBlockM;
+  LoopCtx cx;
+  cx.qw0 = q0 + wave * kRowsPerWave;
+  cx.qrow = cx.qw0 + (lane & 31);
+  cx.diag = p.Nk - p.Nq;
+  cx.Nk = p.Nk;
+  cx.half = lane >> 5;
+  cx.c = p.c;
+  cx.wave_kend = CAUSAL ? cx.qw0 + kRowsPerWave - 1 + cx.diag : p.Nk;
+  int kend = p.Nk;
+  if (CAUSAL) kend = min(p.Nk, q0 + kBlockM + cx.diag);
+  const int nt = kend > 0 ? (kend + kBlockN - 1) / kBlockN : 0;
+  cx.nt = nt;
+
+  const uint32_t head_bytes = (uint32_t)p.Nk * kRowBytes;
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(p.k + (size_t)bh * p.Nk * kRowBytes, head_bytes);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(p.v + (size_t)bh * p.Nk * kRowBytes, head_bytes);
+  TileLoader<D, DT, kWaves> ld;
+  ld.init(wave, lane);
+  WaveState16<D, DT> st;
+  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane);
+
+  if (nt > 0) {
+    // K_1 is loaded even when there is no tile 1 (zeros past the end), so
+    // every K stage an MFMA half reads holds finite data.
+    ld.load(K0, Kr, 0);
+    ld.load(V0, Vr, 0);
+    ld.load(K1, Kr, kBlockN);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    f32x16 s0, s1;
+    i16x8 pf[4];
+    const int tb = first_bias_tile<CAUSAL>(cx);
+    if (grp == 1) __syncthreads();
+    // MFMA half -1: S_0 only
+    if (tb > 0) pp_mfma_half<D, DT, CAUSAL, false, false>(st, cx, -1, pf, s0, s1, K0, V0);
+    else pp_mfma_half<D, DT, CAUSAL, true, false>(st, cx, -1, pf, s0, s1, K0, V0);
+    __syncthreads();
+    // Halves softmax(j), MFMA(j), softmax(j+1), MFMA(j+1) for even j;
+    // returns false after the last MFMA half.
+    auto four_halves = [&](int j, auto masked) -> bool {
+      constexpr bool M = decltype(masked)::value;
+      // softmax(j); B loads K_{j+2} -> K0, V_{j+1} -> V1
+      if (grp == 1) {
+        if (j + 2 < nt) ld.load(K0, Kr, (j + 2) * kBlockN);
+        if (j + 1 < nt) ld.load(V1, Vr, (j + 1) * kBlockN);
+      }
+      pp_softmax_half<D, DT>(st, cx, s0, s1, pf);
+      if (grp == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      // MFMA(j): P_j V_j (V0), S_{j+1} (K1); A loads as B did above
+      if (grp == 0) {
+        if (j + 2 < nt) ld.load(K0, Kr, (j + 2) * kBlockN);
+        if (j + 1 < nt) ld.load(V1, Vr, (j + 1) * kBlockN);
+      }
+      pp_mfma_half<D, DT, CAUSAL, M, true>(st, cx, j, pf, s0, s1, K1, V0);
+      if (grp == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (j + 1 >= nt) return false;
+      // softmax(j+1); B loads K_{j+3} -> K1, V_{j+2} -> V0
+      if (grp == 1) {
+        if (j + 3 < nt) ld.load(K1, Kr, (j + 3) * kBlockN);
+        if (j + 2 < nt) ld.load(V0, Vr, (j + 2) * kBlockN);
+      }
+      pp_softmax_half<D, DT>(st, cx, s0, s1, pf);
+      if (grp == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      // MFMA(j+1): P_{j+1} V_{j+1} (V1), S_{j+2} (K0)
+      if (grp == 0) {
+        if (j + 3 < nt) ld.load(K1, Kr, (j + 3) * kBlockN);
+        if (j + 2 < nt) ld.load(V0, Vr, (j + 2) * kBlockN);
+      }
+      pp_mfma_half<D, DT, CAUSAL, M, true>(st, cx, j + 1, pf, s0, s1, K0, V1);
+      if (grp == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      return j + 2 < nt;
+    };
+    // The MFMA halves of a pair score tiles j+1 and j+2: unmasked while both
+    // lie before the first tile that needs a mask bias.
+    int j = 0;
+    for (; j + 2 < tb; j += 2) four_halves(j, BoolTag<false>{});
+    for (; j < nt; j += 2)
+      if (!four_halves(j, BoolTag<true>{})) break;
+    if (grp == 0) __syncthreads();
+  }
+  store_output<D, DT>(p, st, bh, cx.qrow, cx.half);
+}
+
+// ---------------------------------------------------------------------------
 // Sequential-step kernel: the same tile loop without software pipelining of
 // the scores.  Each step computes S_j, its softmax and O += P_j V_j in
 // order; the overlap of matrix work and softmax comes from the other wave
@@ -1263,6 +1452,7 @@ template <int D, int DT>
 struct Variants {
   static constexpr bool pipelined = D != 256;
   static constexpr bool split = UseSplit<D, DT>::value;
+  static constexpr bool pingpong = D == 128 && DT != ATTN_FP8_E4M3;
 };
 
 // ---------------------------------------------------------------------------
@@ -1321,6 +1511,12 @@ int launch_one(const Problem& pr, hipStream_t stream) {
     case ATTN_VARIANT_PIPELINED_4STAGE:
       if constexpr (Variants<D, DT>::pipelined) {
         hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL, 4>), dim3(p.total_tiles), block, 0, stream, p);
+        break;
+      }
+      return ATTN_ERR_VARIANT;
+    case ATTN_VARIANT_PINGPONG:
+      if constexpr (Variants<D, DT>::pingpong) {
+        hipLaunchKernelGGL((attn_fwd_pingpong_kernel<D, DT, CAUSAL>), dim3(p.total_tiles), block, 0, stream, p);
         break;
       }
       return ATTN_ERR_VARIANT;

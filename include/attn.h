@@ -91,13 +91,18 @@ enum {
  *                      barrier per two key tiles (d = 64, 128)
  *   SEQUENTIAL         one key tile per step, no score pipelining (all d)
  *   SPLIT              two wave groups over the two halves of the key range,
- *                      merged at the end (16-bit d = 64) */
+ *                      merged at the end (16-bit d = 64)
+ *   PINGPONG           two wave groups alternating matrix-only and
+ *                      softmax-only halves of each step behind workgroup
+ *                      barriers, so that one group's softmax runs under the
+ *                      other's MFMAs (16-bit d = 128) */
 enum {
   ATTN_VARIANT_AUTO = 0,
   ATTN_VARIANT_PIPELINED = 1,
   ATTN_VARIANT_PIPELINED_4STAGE = 2,
   ATTN_VARIANT_SEQUENTIAL = 3,
-  ATTN_VARIANT_SPLIT = 4
+  ATTN_VARIANT_SPLIT = 4,
+  ATTN_VARIANT_PINGPONG = 5
 };
 
 /*

@@ -43,7 +43,8 @@
 //     walk the two halves of the key range and merge.
 // Those are the defaults (launch_one).  Every kernel built for a (d,
 // format) can also be requested explicitly as a tuning variant, including
-// the pipelined kernel with a four-stage K/V ring.
+// the pipelined kernel with a four-stage K/V ring and, at 16-bit d = 128,
+// attn_fwd_pingpong_kernel: the pages' explicit two-group pingpong.
 // Masking is folded into the initial values of the score accumulators; the
 // key loops run the unmasked steps and the masked ones (ragged end, causal
 // diagonal) as two loops of one step variant each, so every step is one

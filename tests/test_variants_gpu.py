@@ -21,7 +21,7 @@ CASES = [(d, dt, var) for d in (64, 128, 256) for dt in ("f16", "bf16", "e4m3") 
          if attn_variant_available(d, CODES[dt], var)]
 
 
-@pytest.mark.parametrize("nq,nk", [(300, 300), (129, 520), (700, 64)])
+@pytest.mark.parametrize("nq,nk", [(300, 300), (129, 520), (700, 64), (150, 150)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d,dtype,variant", CASES, ids=[f"d{d}-{t}-{VARIANT_NAMES[v]}" for d, t, v in CASES])
 def test_variant_parity(d, dtype, variant, causal, nq, nk):

@@ -36,9 +36,12 @@ def _cpu_baseline(inp, budget_s, smoothed=False):
     workload's heads, in order, until about `budget_s` seconds of CPU work
     (for the smoothed FP8 workload including the quantisation of each head)."""
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in pools] or [1])
+        blas = ", ".join(sorted({str(i.get("internal_api")) for i in pools})) or "unknown"
     except Exception:  # threadpoolctl missing: report the affinity set
         threads = len(os.sched_getaffinity(0))
     dec = {"f16": oracle.decode_f16, "bf16": oracle.decode_bf16, "e4m3": oracle.decode_e4m3}[inp.dtype]
@@ -86,6 +89,8 @@ def _cpu_baseline(inp, budget_s, smoothed=False):
         "value": flops / spent / 1e12,
         "unit": "TFLOPs/s",
         "cores": int(threads),
+        "affinity_cores": len(os.sched_getaffinity(0)),
+        "blas": blas,
         "kind": "oracle",
         "sample": (f"{done_rows} query rows ({chunk}-row chunks) of {heads} of {inp.B * inp.H} heads, "
                    f"{spent:.1f} s, float64 numpy oracle, same FLOP count convention"
@@ -202,7 +207,8 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    kernel_ms = sum(a.elapsed_time(b) for a, b in marks) / len(marks)
+    launch_ms = sorted(a.elapsed_time(b) for a, b in marks)
+    kernel_ms = sum(launch_ms) / len(launch_ms)
 
     fl = inputs.flops(inp.B, inp.H, inp.Nq, inp.Nk, inp.d, inp.causal)
     tflops = fl / (ms * 1e-3) / 1e12
@@ -233,7 +239,9 @@ def main():
                      "frac": round(kernel_tflops / peak, 4), "traffic": tr["bytes"] if tr else None,
                      "traffic_unit": "bytes per launch (HBM read + write)",
                      "kernel": tr["kernel"] if tr else "attn_fwd", "flops_per_launch": fl,
-                     "kernel_ms": round(kernel_ms, 4)},
+                     "kernel_ms": round(kernel_ms, 4),
+                     "kernel_ms_median": round(launch_ms[len(launch_ms) // 2], 4),
+                     "kernel_ms_min": round(launch_ms[0], 4)},
     }
     if smoothed:
         rec["config"]["path"] = ("block-scaled E4M3, 64-row blocks; Q and K 16x16 Walsh-Hadamard smoothed; "

@@ -56,6 +56,8 @@ bool variant_available(int d, int dtype, int variant) {
       return d == 64 && dtype != ATTN_FP8_E4M3;
     case ATTN_VARIANT_PINGPONG:
       return d == 128 && dtype != ATTN_FP8_E4M3;
+    case ATTN_VARIANT_PRODUCER:
+      return d == 128;
     default:
       return false;
   }

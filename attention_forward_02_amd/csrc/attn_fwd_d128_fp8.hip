@@ -17,6 +17,8 @@ template __global__ void attn_fwd_kernel<128, ATTN_FP8_E4M3, false>(Params);
 template __global__ void attn_fwd_kernel<128, ATTN_FP8_E4M3, true>(Params);
 template __global__ void attn_fwd_kernel<128, ATTN_FP8_E4M3, false, 4>(Params);
 template __global__ void attn_fwd_kernel<128, ATTN_FP8_E4M3, true, 4>(Params);
+template __global__ void attn_fwd_producer_kernel<128, ATTN_FP8_E4M3, false, 2, 1>(Params);
+template __global__ void attn_fwd_producer_kernel<128, ATTN_FP8_E4M3, true, 2, 1>(Params);
 
 }  // namespace kernels
 

@@ -5,7 +5,8 @@ attention shape on the GPU and list them fastest first.
 
 The variants (ATTN_VARIANT_* in include/attn.h) compute the same forward pass
 with different schedules: the pipelined kernel with a two- or four-stage K/V
-ring, the sequential kernel, and the split-key kernel.  The pages choose
+ring, the sequential kernel, the split-key kernel, the pingpong kernel and
+the producer-wave kernel.  The pages choose
 tiles and stage counts by profiling ("Warp specialization" concept card, its
 notes on tile sizes and on the three-stage variants); this does the same on
 the device at hand.  The library's default (ATTN_VARIANT_AUTO) encodes the
@@ -35,7 +36,8 @@ from . import binding as b
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 VARIANTS = [b.ATTN_VARIANT_AUTO, b.ATTN_VARIANT_PIPELINED, b.ATTN_VARIANT_PIPELINED_4STAGE,
-            b.ATTN_VARIANT_SEQUENTIAL, b.ATTN_VARIANT_SPLIT, b.ATTN_VARIANT_PINGPONG]
+            b.ATTN_VARIANT_SEQUENTIAL, b.ATTN_VARIANT_SPLIT, b.ATTN_VARIANT_PINGPONG,
+            b.ATTN_VARIANT_PRODUCER]
 
 
 def _agree(o, lse, o_ref, lse_ref, fp8):

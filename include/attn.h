@@ -95,14 +95,18 @@ enum {
  *   PINGPONG           two wave groups alternating matrix-only and
  *                      softmax-only halves of each step behind workgroup
  *                      barriers, so that one group's softmax runs under the
- *                      other's MFMAs (16-bit d = 128) */
+ *                      other's MFMAs (16-bit d = 128)
+ *   PRODUCER           a ninth, producer wave streams K and V into a
+ *                      2-stage ring; the eight consumer waves run the
+ *                      sequential step on tiles already in LDS (d = 128) */
 enum {
   ATTN_VARIANT_AUTO = 0,
   ATTN_VARIANT_PIPELINED = 1,
   ATTN_VARIANT_PIPELINED_4STAGE = 2,
   ATTN_VARIANT_SEQUENTIAL = 3,
   ATTN_VARIANT_SPLIT = 4,
-  ATTN_VARIANT_PINGPONG = 5
+  ATTN_VARIANT_PINGPONG = 5,
+  ATTN_VARIANT_PRODUCER = 6
 };
 
 /*

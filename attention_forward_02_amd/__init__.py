@@ -28,6 +28,7 @@ from .binding import (  # noqa: F401
     ATTN_VARIANT_PRODUCER,
     ATTN_VARIANT_SEQUENTIAL,
     ATTN_VARIANT_SPLIT,
+    ATTN_VARIANT_WIDE,
     VARIANT_NAMES,
     AttnError,
     ATTN_FP8_BLOCK_ROWS,

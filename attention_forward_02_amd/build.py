@@ -46,6 +46,9 @@ SOURCES = [
     ("attn_dispatch.cpp", []),
     ("attn_fwd_d64.hip", VGPR_FORM),
     ("attn_fwd_d128.hip", VGPR_FORM + TRACKERS),
+    # 64 rows per wave, one wave per SIMD: the default (AGPR) form keeps the
+    # output accumulators in AGPRs.
+    ("attn_fwd_d128_wide.hip", []),
     ("attn_fwd_d256.hip", VGPR_FORM),
     ("attn_fwd_d64_fp8.hip", VGPR_FORM),
     ("attn_fwd_d128_fp8.hip", VGPR_FORM),

@@ -58,6 +58,8 @@ bool variant_available(int d, int dtype, int variant) {
       return d == 128 && dtype != ATTN_FP8_E4M3;
     case ATTN_VARIANT_PRODUCER:
       return d == 128;
+    case ATTN_VARIANT_WIDE:
+      return d == 128 && dtype != ATTN_FP8_E4M3;
     default:
       return false;
   }

@@ -29,8 +29,11 @@
 //   * exp is v_exp_f32 (2^x) on scores pre-multiplied by scale * log2(e);
 //     LSE is converted back to natural log at the end.
 //
-// Three kernels share these pieces:
-//   * attn_fwd_kernel (16-bit d = 64 and 128, E4M3 d = 64): each step
+// Four kernels share these pieces:
+//   * attn_fwd_producer_kernel (binary16 d = 128): eight consumer waves run
+//     the sequential step below while a ninth, producer wave streams K and
+//     V into the LDS ring;
+//   * attn_fwd_kernel (bfloat16 d = 128, 16-bit d = 64, E4M3 d = 64): each step
 //     overlaps the score MFMAs of the next tile with the exponentials of the
 //     current one, and the P V MFMAs with the row sums and the next tile's
 //     row max (the pages' two-stage overlap of matrix multiplies and
@@ -45,7 +48,8 @@
 // format) can also be requested explicitly as a tuning variant, including
 // the pipelined kernel with a four-stage K/V ring and, at 16-bit d = 128,
 // attn_fwd_pingpong_kernel (the pages' explicit two-group pingpong) and
-// attn_fwd_producer_kernel (a dedicated producer wave).
+// attn_fwd_wide_kernel (64 query rows per wave, one wave per SIMD;
+// attn_fwd_wide.h, its own translation unit).
 // Masking is folded into the initial values of the score accumulators; the
 // key loops run the unmasked steps and the masked ones (ragged end, causal
 // diagonal) as two loops of one step variant each, so every step is one
@@ -1565,7 +1569,12 @@ struct Variants {
   static constexpr bool split = UseSplit<D, DT>::value;
   static constexpr bool pingpong = D == 128 && DT != ATTN_FP8_E4M3;
   static constexpr bool producer = D == 128;
+  static constexpr bool wide = D == 128 && DT != ATTN_FP8_E4M3;
 };
+
+// The wide-wave kernels (attn_fwd_wide.h) live in a translation unit of
+// their own, built with the compiler's default MFMA register form.
+int launch_wide_d128(const Params& p, int dtype, bool causal, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Launch
@@ -1639,6 +1648,9 @@ int launch_one(const Problem& pr, hipStream_t stream) {
                            stream, p);
         break;
       }
+      return ATTN_ERR_VARIANT;
+    case ATTN_VARIANT_WIDE:
+      if constexpr (Variants<D, DT>::wide) return launch_wide_d128(p, DT, CAUSAL, stream);
       return ATTN_ERR_VARIANT;
     default:
       return ATTN_ERR_VARIANT;

@@ -98,7 +98,11 @@ enum {
  *                      other's MFMAs (16-bit d = 128)
  *   PRODUCER           a ninth, producer wave streams K and V into a
  *                      2-stage ring; the eight consumer waves run the
- *                      sequential step on tiles already in LDS (d = 128) */
+ *                      sequential step on tiles already in LDS (d = 128)
+ *   WIDE               64 query rows per wave (two 32-row blocks sharing
+ *                      every K and V operand read), one wave per SIMD with
+ *                      the output accumulators in AGPRs, pipelined steps
+ *                      (16-bit d = 128) */
 enum {
   ATTN_VARIANT_AUTO = 0,
   ATTN_VARIANT_PIPELINED = 1,
@@ -106,7 +110,8 @@ enum {
   ATTN_VARIANT_SEQUENTIAL = 3,
   ATTN_VARIANT_SPLIT = 4,
   ATTN_VARIANT_PINGPONG = 5,
-  ATTN_VARIANT_PRODUCER = 6
+  ATTN_VARIANT_PRODUCER = 6,
+  ATTN_VARIANT_WIDE = 7
 };
 
 /*

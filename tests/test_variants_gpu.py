@@ -17,7 +17,7 @@ from gpu_helpers import compare, dequant, fp8_lse_tol, say, upload
 pytestmark = pytest.mark.gpu
 
 CODES = {"f16": ATTN_F16, "bf16": ATTN_BF16, "e4m3": ATTN_FP8_E4M3}
-CASES = [(d, dt, var) for d in (64, 128, 256) for dt in ("f16", "bf16", "e4m3") for var in (1, 2, 3, 4, 5, 6)
+CASES = [(d, dt, var) for d in (64, 128, 256) for dt in ("f16", "bf16", "e4m3") for var in (1, 2, 3, 4, 5, 6, 7)
          if attn_variant_available(d, CODES[dt], var)]
 
 

@@ -246,7 +246,99 @@ def summarize(outdir, workload):
           f"kernel avg {avg_ns / 1e3:.1f} us; MFMA busy {100 * mfma_busy:.1f} %")
 
 
+# Counter passes of profile_variants.sh: wave states, then issue counts.
+VARIANT_PASSES = [
+    ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+     "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE"],
+    ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_LDS_LOAD_BANDWIDTH",
+     "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE"],
+]
+
+
+def _per_kernel(path):
+    """Per-dispatch mean of every counter, per attention kernel
+    instantiation (the name up to its template arguments)."""
+    agg = defaultdict(lambda: defaultdict(float))
+    disp = defaultdict(set)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if KERNEL not in name:
+                continue
+            key = name.split("attn::kernels::")[1].split("(")[0]
+            agg[key][r["Counter_Name"]] += float(r["Counter_Value"])
+            disp[key].add(r["Dispatch_Id"])
+    return {k: {c: v / len(disp[k]) for c, v in d.items()} for k, d in agg.items()}
+
+
+def summarize_variants(outdir, workload):
+    """profiles/variants_<workload>.md: the counters of every kernel variant
+    on one workload, from profile_variants.sh's passes over the tuner."""
+    stats = {}
+    with open(_one(os.path.join(outdir, "trace", "**", "*kernel_stats.csv"))) as f:
+        for r in csv.DictReader(f):
+            if KERNEL in r["Name"]:
+                stats[r["Name"].split("attn::kernels::")[1].split("(")[0]] = float(r["AverageNs"])
+    c = defaultdict(dict)
+    for i in range(1, len(VARIANT_PASSES) + 1):
+        for k, v in _per_kernel(_one(os.path.join(outdir, f"pmc{i}", "**", "*counter_collection.csv"))).items():
+            c[k].update(v)
+    tune = f"python3 -m attention_forward_02_amd.tune --workload {workload} --reps 3 --rounds 1"
+    lines = [
+        f"# Counters of every kernel variant on {workload}",
+        "",
+        f"Kernel sources digest: `{kernel_digest()}` (code only: comments and whitespace aside)",
+        "",
+        "Made by (from the repository root, on one MI355X):",
+        "",
+        "```",
+        f"bash attention_forward_02_amd/profile_variants.sh {workload} {outdir}",
+        f"python -m attention_forward_02_amd.profiling --variants {outdir} {workload}",
+        "```",
+        "",
+        "which runs, each under its own time limit:",
+        "",
+        "```",
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d {outdir}/trace -o run -- {tune}",
+    ]
+    for i, names in enumerate(VARIANT_PASSES, 1):
+        lines.append(f"rocprofv3 --pmc {' '.join(names)} --output-format csv -d {outdir}/pmc{i} -o run -- {tune}")
+    lines += [
+        "```",
+        "",
+        "Per dispatch, averaged over the tuner's launches of each kernel.  Wave-state",
+        "fractions are of SQ_WAVE_CYCLES (every resident wave, a producer wave",
+        "included): waiting = SQ_WAIT_ANY (on a waitcnt or a barrier), ready =",
+        "SQ_WAIT_INST_ANY (an instruction ready but not issued), issuing =",
+        "SQ_ACTIVE_INST_ANY.  LDS bytes from SQ_INSTS_LDS_LOAD_BANDWIDTH (64-byte",
+        "units) over the kernel cycles and 256 CUs.",
+        "",
+        "| kernel | avg us (trace) | MFMA busy | waiting | ready | issuing | VALU instr / MFMA | LDS instr / MFMA "
+        "| LDS read B/clk per CU | bank conflicts |",
+        "|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    for k in sorted(c, key=lambda k: stats.get(k, 1e30)):
+        x = c[k]
+        cyc = x["GRBM_GUI_ACTIVE"] / N_XCD
+        wc = x["SQ_WAVE_CYCLES"]
+        mf = max(1.0, x["SQ_INSTS_MFMA"])
+        avg = f"{stats[k] / 1e3:.1f}" if k in stats else "-"
+        lines.append(
+            f"| `{k}` | {avg} | {100 * x['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * N_SIMD):.1f}% "
+            f"| {100 * x['SQ_WAIT_ANY'] / wc:.1f}% | {100 * x['SQ_WAIT_INST_ANY'] / wc:.1f}% "
+            f"| {100 * x['SQ_ACTIVE_INST_ANY'] / wc:.1f}% | {x['SQ_INSTS_VALU'] / mf:.2f} | {x['SQ_INSTS_LDS'] / mf:.2f} "
+            f"| {x['SQ_INSTS_LDS_LOAD_BANDWIDTH'] * 64 / 256 / cyc:.1f} | {x['SQ_LDS_BANK_CONFLICT']:.0f} |")
+    lines.append("")
+    md = os.path.join(PROFILES, f"variants_{workload}.md")
+    with open(md, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {md}")
+
+
 if __name__ == "__main__":
-    if len(sys.argv) != 3:
+    if len(sys.argv) == 4 and sys.argv[1] == "--variants":
+        summarize_variants(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) == 3:
+        summarize(sys.argv[1], sys.argv[2])
+    else:
         sys.exit(__doc__)
-    summarize(sys.argv[1], sys.argv[2])

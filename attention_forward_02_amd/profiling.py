@@ -45,6 +45,7 @@ KERNEL = "attn::kernels::attn_fwd"  # every kernel of the library
 N_XCD = 8
 N_SIMD = 1024
 COPY_BYTES = 1 << 30
+HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
 
 PMC_PASSES = [
     ["FETCH_SIZE"],
@@ -210,6 +211,9 @@ def summarize(outdir, workload):
         f"| copy calibration WRITE_SIZE (1 GiB written) | {copy['WRITE_SIZE']:.6g} KiB -> factor {f_write:.4f} |",
         f"| HBM read per launch (calibrated) | {fetch_b / 1e6:.1f} MB |",
         f"| HBM write per launch (calibrated) | {write_b / 1e6:.1f} MB |",
+        f"| HBM bandwidth (read + write per launch / average kernel time) | "
+        f"{(fetch_b + write_b) / (avg_ns * 1e-9) / 1e9:.0f} GB/s, "
+        f"{100 * (fetch_b + write_b) / (avg_ns * 1e-9) / HBM_PEAK:.1f} % of 8 TB/s |",
     ]
     if alg_read is not None:
         lines.append(f"| algorithmic read (Q, K, V once) / write (O, LSE) | {alg_read / 1e6:.1f} MB / "

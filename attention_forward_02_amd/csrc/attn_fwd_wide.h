@@ -119,7 +119,7 @@ __device__ __forceinline__ float wide_row_sum(const f32x16* s, const i16x8 (&pf)
   }
 }
 
-// Instruction interleave of 2 NP MFMAs: after `pre` LDS reads, pairs of
+// Instruction interleave of np MFMA pairs: after `pre` LDS reads, pairs of
 // MFMAs with `valu` VALU or transcendental instructions after each and
 // `reads` LDS reads after the first (mask 0x402: v_exp_f32 is not in the
 // plain VALU class); then the end of the scheduling region.

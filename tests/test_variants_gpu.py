@@ -2,7 +2,9 @@
 oracle, with the tolerances of tests/gpu_helpers.py, and the tuner on a small
 shape.  Shapes are ragged (N = 300: four full 64-key tiles and a partial one;
 Nq != Nk) so every variant's masked steps and ring turns are exercised, for
-every head dim, input format and causality the variant is built for."""
+every head dim, input format and causality the variant is built for; every
+d = 128 variant also at the full B=2 H=16 N=8192 size (fp16 and E4M3), on
+sampled rows."""
 
 import numpy as np
 import pytest
@@ -53,3 +55,43 @@ def test_tuner_times_every_variant():
     timed = [r["ms"] for r in rows[1:]]
     assert timed == sorted(timed)
     say("[gpu] tuner: " + ", ".join(f"{r['name']} {r['ms']:.4f} ms" for r in rows))
+
+
+_FULL = {}
+
+
+def _full_workload(name):
+    """Inputs and uploaded tensors of a full-size workload, made once per
+    module."""
+    if name not in _FULL:
+        inp = inputs.make_workload(name)
+        q, k, v = (upload(t, inp.dtype) for t in (inp.q, inp.k, inp.v))
+        _FULL[name] = (inp, q, k, v)
+    return _FULL[name]
+
+
+FULL_CASES = [(wl, var) for wl, dt in (("hd128_seq8k_f16", "f16"), ("hd128_seq8k_e4m3", "e4m3"))
+              for var in (1, 2, 3, 4, 5, 6, 7) if attn_variant_available(128, CODES[dt], var)]
+
+
+@pytest.mark.parametrize("workload,variant", FULL_CASES, ids=[f"{w}-{VARIANT_NAMES[v]}" for w, v in FULL_CASES])
+def test_variant_full_size_sampled(workload, variant):
+    """Every d = 128 variant at the full B=2 H=16 N=8192 size, against the
+    oracle on sampled rows of two heads (the first and the last)."""
+    label = f"variant {VARIANT_NAMES[variant]} {workload}"
+    say(f"[gpu] {label}: B=2 H=16 N=8192 d=128 (sampled)")
+    inp, q, k, v = _full_workload(workload)
+    desc = tuple(float(x) for x in inp.descale) if inp.dtype == "e4m3" else None
+    o, lse = attention(q, k, v, causal=False, scale=float(inp.scale), descale=desc, variant=variant)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (1, 15)]
+    rng = np.random.default_rng(variant)
+    rows = np.unique(np.concatenate([[0, 63, 64, 255, 256, inp.Nq - 1], rng.choice(inp.Nq, 24, replace=False)]))
+    idx = torch.as_tensor(rows, device=o.device)
+    o_sel = np.stack([o[b, h][idx].view(torch.int16).cpu().numpy().view(np.uint16) for b, h in heads])[None]
+    l_sel = np.stack([lse[b, h][idx].cpu().numpy() for b, h in heads])[None]
+    qq, kk, vv = dequant(inp, heads)
+    o_ref, lse_ref = oracle.attention(qq, kk, vv, False, float(inp.scale), rows=rows)
+    ltol = fp8_lse_tol(qq, kk, float(inp.scale))[:, :, rows] if inp.dtype == "e4m3" else None
+    stats = compare(o_sel, l_sel, o_ref, lse_ref, inp.dtype, label, lse_tol=ltol)
+    say(f"[gpu] {label}: {stats}")

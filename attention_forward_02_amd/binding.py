@@ -164,6 +164,51 @@ def _dtype_code(t):
     raise TypeError(f"unsupported input dtype {t.dtype}")
 
 
+def _check_device(tensors, names):
+    """Every tensor on one GPU: the library dereferences raw device pointers,
+    so a host tensor or a second device must be refused here."""
+    dev = None
+    for t, n in zip(tensors, names):
+        if not getattr(t, "is_cuda", False):
+            raise ValueError(f"{n} must be a GPU tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{n} is on {t.device}, expected {dev}")
+
+
+def _check_qkv(q, k, v, placement=True):
+    """Shapes, dtypes and placement of q [B,H,Nq,d], k and v [B,H,Nk,d]:
+    the C ABI sees only pointers and sizes, so a K or V smaller than the sizes
+    taken from q would be read past its end on the device."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dim() != 4:
+            raise ValueError(f"{n} must be 4-D [B, H, N, d], got shape {tuple(t.shape)}")
+    if tuple(k.shape[:2]) != tuple(q.shape[:2]) or k.shape[3] != q.shape[3]:
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)} in B, H or d")
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v {tuple(v.shape)} must have k's shape {tuple(k.shape)}")
+    code = _dtype_code(q)
+    if _dtype_code(k) != code or _dtype_code(v) != code:
+        raise TypeError("q, k, v must share one dtype")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if placement:
+        _check_device((q, k, v), ("q", "k", "v"))
+
+
+def _check_descales(ds, name, B, H, N):
+    import torch
+    nb = (N + ATTN_FP8_BLOCK_ROWS - 1) // ATTN_FP8_BLOCK_ROWS
+    if tuple(ds.shape) != (B, H, nb):
+        raise ValueError(f"{name} must have shape {(B, H, nb)}, got {tuple(ds.shape)}")
+    if ds.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    if not ds.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def attention(q, k, v, causal=False, scale=None, descale=None, stream=None, variant=None):
     """O, LSE for contiguous device tensors q [B,H,Nq,d], k, v [B,H,Nk,d].
 
@@ -174,14 +219,10 @@ def attention(q, k, v, causal=False, scale=None, descale=None, stream=None, vari
     kernel variant through ``attn_fwd_variant``; None runs the default.
     """
     import torch
+    _check_qkv(q, k, v)
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     code = _dtype_code(q)
-    if _dtype_code(k) != code or _dtype_code(v) != code:
-        raise TypeError("q, k, v must share one dtype")
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out_dtype = torch.bfloat16 if code == ATTN_BF16 else torch.float16
@@ -206,10 +247,15 @@ def quantize_fp8(x, hadamard=False, stream=None):
     [B,H,ceil(N/64)]), optionally after the 16x16 Walsh-Hadamard transform
     (for Q and K only)."""
     import torch
+    if x.dim() != 4:
+        raise ValueError(f"x must be 4-D [B, H, N, d], got shape {tuple(x.shape)}")
+    code = _dtype_code(x)
+    if code == ATTN_FP8_E4M3:
+        raise TypeError("x must be float16 or bfloat16")
     if not x.is_contiguous():
         raise ValueError("x must be contiguous")
+    _check_device((x,), ("x",))
     B, H, N, d = x.shape
-    code = _dtype_code(x)
     nb = (N + ATTN_FP8_BLOCK_ROWS - 1) // ATTN_FP8_BLOCK_ROWS
     codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
     descales = torch.empty((B, H, nb), dtype=torch.float32, device=x.device)
@@ -223,11 +269,16 @@ def attention_fp8_blockscaled(q, k, v, q_descales, k_descales, v_descales, causa
     """O (fp16), LSE for block-scaled E4M3 codes (uint8 or float8_e4m3fn
     device tensors [B,H,N,d]) and their float32 descales [B,H,ceil(N/64)]."""
     import torch
+    _check_qkv(q, k, v, placement=False)
+    if _dtype_code(q) != ATTN_FP8_E4M3:
+        raise TypeError("q, k, v must be E4M3 codes (uint8 or float8_e4m3fn)")
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
-    for t in (q, k, v, q_descales, k_descales, v_descales):
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous")
+    _check_descales(q_descales, "q_descales", B, H, Nq)
+    _check_descales(k_descales, "k_descales", B, H, Nk)
+    _check_descales(v_descales, "v_descales", B, H, Nk)
+    _check_device((q, k, v, q_descales, k_descales, v_descales),
+                  ("q", "k", "v", "q_descales", "k_descales", "v_descales"))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty((B, H, Nq, d), dtype=torch.float16, device=q.device)

@@ -70,10 +70,10 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   int st = validate(q, k, v, o, lse, B, H, Nq, Nk, d, dtype);
   if (st != ATTN_OK) return st;
   if (!variant_available(d, dtype, variant)) return ATTN_ERR_VARIANT;
-  if (!positive_finite(scale) || !positive_finite(q_ds) || !positive_finite(k_ds) || !positive_finite(v_ds))
+  if (!isfinite(scale) || !positive_finite(q_ds) || !positive_finite(k_ds) || !positive_finite(v_ds))
     return ATTN_ERR_SCALE;
   const float s = scale * q_ds * k_ds;
-  if (!positive_finite(s)) return ATTN_ERR_SCALE;
+  if (!isfinite(s)) return ATTN_ERR_SCALE;
   attn::Problem p;
   p.q = q;
   p.k = k;
@@ -160,7 +160,7 @@ int attn_fwd_fp8_blockscaled(const void* q, const void* k, const void* v, const 
   const size_t dsb[3] = {qdb, kdb, kdb};
   for (int i = 0; i < 3; ++i)
     if (overlap(o, ob, ds[i], dsb[i]) || overlap(lse, lb, ds[i], dsb[i])) return ATTN_ERR_ALIAS;
-  if (!positive_finite(scale)) return ATTN_ERR_SCALE;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
   attn::Problem p;
   p.q = q;
   p.k = k;
@@ -193,7 +193,7 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_DTYPE: return "unknown dtype";
     case ATTN_ERR_ALIGN:
       return "q, k, v, o (x, codes) must be 16-byte aligned and lse (descales) 4-byte aligned";
-    case ATTN_ERR_SCALE: return "scale and descales must be finite and > 0";
+    case ATTN_ERR_SCALE: return "scale must be finite, and descales finite and > 0";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case ATTN_ERR_VARIANT: return "unknown kernel variant, or not built for this head dim and dtype";

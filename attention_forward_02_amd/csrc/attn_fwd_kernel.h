@@ -105,7 +105,12 @@ struct Params {
   int Nq, Nk;
   int n_qtiles;     // ceil(Nq / query rows per workgroup)
   int total_tiles;  // B * H * n_qtiles
-  float c;          // scale * log2(e): scores -> base-2 exponent units
+  float c;          // |scale| * log2(e): scores -> base-2 exponent units (> 0)
+  // Applied to every 32-bit word of Q as it is loaded, (w & q_and) ^ q_xor:
+  // the sign bits flipped for a negative scale (so that c stays positive and
+  // the -inf mask bias keeps its meaning), all bits cleared for a zero scale
+  // (every score is then exactly 0), else unchanged.
+  uint32_t q_and, q_xor;
   float o_scale;    // multiplies P V (the v descale for E4M3, else 1)
   // Block-scaled E4M3 only: descales of 64-row blocks, [B*H][nqb] for Q and
   // [B*H][nkb] for K and V (one K/V block per key tile).
@@ -291,12 +296,14 @@ struct WaveState16 {
   int koff[kKOff];        // per-lane LDS byte offsets of K operand reads
   int voff[4][2];         // per-lane LDS byte offsets of V transpose reads
 
-  __device__ __forceinline__ void init(const unsigned char* Qb, int qrow, int Nq, int lane) {
+  __device__ __forceinline__ void init(const unsigned char* Qb, int qrow, int Nq, int lane, uint32_t q_and,
+                                       uint32_t q_xor) {
     const int half = lane >> 5, r32 = lane & 31;
     // Q rows of this lane: chunk (2s + half) of the row, clamped for rows past Nq.
     const i16x8* src = (const i16x8*)(Qb + (size_t)min(qrow, Nq - 1) * kRowBytes);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = src[2 * s + half];
+    for (int s = 0; s < D / 16; ++s)
+      qf[s] = __builtin_bit_cast(i16x8, (__builtin_bit_cast(u32x4, src[2 * s + half]) & q_and) ^ q_xor);
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
     m2 = -__builtin_inff();
@@ -339,13 +346,15 @@ struct WaveState8 {
   int koff[D / 32];       // K operand reads: two 16-byte chunks per k-step
   int voff[D / 32];       // V transpose reads: one offset per 32-column block
 
-  __device__ __forceinline__ void init(const unsigned char* Qb, int qrow, int Nq, int lane) {
+  __device__ __forceinline__ void init(const unsigned char* Qb, int qrow, int Nq, int lane, uint32_t q_and,
+                                       uint32_t q_xor) {
     const int half = lane >> 5, r32 = lane & 31;
     const i32x4* src = (const i32x4*)(Qb + (size_t)min(qrow, Nq - 1) * kRowBytes);
+    const int qa = (int)q_and, qx = (int)q_xor;
 #pragma unroll
     for (int s = 0; s < D / 64; ++s) {
       const i32x4 lo = src[4 * s + 2 * half], hi = src[4 * s + 2 * half + 1];
-      qf[s] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      qf[s] = (__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7) & qa) ^ qx;
     }
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
@@ -830,7 +839,7 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_kernel(Pa
   TileLoader<D, DT, kWaves> ld;
   ld.init(wave, lane);
   WaveState<D, DT> st;
-  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane);
+  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane, p.q_and, p.q_xor);
 
   // Scores (then probabilities) of even tiles live in (a0, a1), of odd
   // tiles in (b0, b1).
@@ -1059,7 +1068,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) a
   TileLoader<D, DT, kWaves> ld;
   ld.init(wave, lane);
   WaveState16<D, DT> st;
-  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane);
+  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane, p.q_and, p.q_xor);
 
   if (nt > 0) {
     // K_1 is loaded even when there is no tile 1 (zeros past the end), so
@@ -1236,7 +1245,7 @@ attn_fwd_seq_kernel(Params p) {
   TileLoader<D, DT, kWaves, BN> ld;
   ld.init(wave, lane);
   WaveState<D, DT> st;
-  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane);
+  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane, p.q_and, p.q_xor);
 
   if (nt > 0) {
     ld.load(K0, Kr, 0);
@@ -1371,7 +1380,7 @@ __global__ void __launch_bounds__(64 * (8 + NP)) attn_fwd_producer_kernel(Params
   cx.wave_kend = CAUSAL ? cx.qw0 + kRowsPerWave - 1 + cx.diag : p.Nk;
   cx.nt = nt;
   WaveState<D, DT> st;
-  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane);
+  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane, p.q_and, p.q_xor);
   const int tb = min(first_bias_tile<CAUSAL>(cx), nt);
   const TileScale ts{};
   // One barrier per step, nt in all, as on the producer side.
@@ -1456,7 +1465,7 @@ __global__ void __launch_bounds__(512) attn_fwd_split_kernel(Params p) {
   TileLoader<D, DT, kGroupWaves> ld;
   ld.init(rb, lane);
   WaveState<D, DT> st;
-  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane);
+  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane, p.q_and, p.q_xor);
 
   // The key loop of one group over tiles [j0, j1), as in attn_fwd_kernel.
   // Every group executes the same number of barriers: 1 + (mid + 1) / 2
@@ -1576,6 +1585,25 @@ struct Variants {
 // their own, built with the compiler's default MFMA register form.
 int launch_wide_d128(const Params& p, int dtype, bool causal, hipStream_t stream);
 
+// Score scaling of a launch.  The kernels need c = scale * log2(e) > 0: the
+// -inf mask bias must stay -inf after the multiply, and the row max must be
+// the max of c * s.  A negative scale is folded into Q instead (its sign
+// bits flipped as Q is loaded: (-Q) K^T is exactly -(Q K^T)), and a zero one
+// (or one whose c underflows to 0) clears Q, so every score is exactly 0 and
+// any c > 0 gives the uniform softmax over the visible keys.
+__host__ inline void set_scale(Params& p, float scale, int dtype) {
+  const uint32_t sign = dtype == ATTN_FP8_E4M3 ? 0x80808080u : 0x80008000u;
+  p.c = fabsf(scale) * kLog2e;
+  p.q_and = 0xffffffffu;
+  p.q_xor = 0u;
+  if (!(p.c > 0.f)) {
+    p.c = 1.f;
+    p.q_and = 0u;
+  } else if (scale < 0.f) {
+    p.q_xor = sign;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
@@ -1595,7 +1623,7 @@ int launch_one(const Problem& pr, hipStream_t stream) {
   const long long total = (long long)pr.B * pr.H * p.n_qtiles;
   if (total > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   p.total_tiles = (int)total;
-  p.c = pr.scale * kLog2e;
+  set_scale(p, pr.scale, DT);
   p.o_scale = pr.v_descale;
   p.qs = p.ks = p.vs = nullptr;
   p.nqb = p.nkb = 0;
@@ -1690,7 +1718,7 @@ int launch_blockscaled(const Problem& pr, hipStream_t stream) {
   const long long total = (long long)pr.B * pr.H * p.n_qtiles;
   if (total > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   p.total_tiles = (int)total;
-  p.c = pr.scale * kLog2e;
+  set_scale(p, pr.scale, ATTN_FP8_E4M3);
   p.o_scale = 1.f;
   p.qs = pr.q_descales;
   p.ks = pr.k_descales;

@@ -233,8 +233,8 @@ attn_fwd_wide_kernel(Params p) {
   ld.init(wave, lane);
   WaveState16<D, DT> x, y;
   const unsigned char* Qh = p.q + (size_t)bh * p.Nq * kRowBytes;
-  x.init(Qh, cx.qrow, p.Nq, lane);
-  y.init(Qh, cy.qrow, p.Nq, lane);
+  x.init(Qh, cx.qrow, p.Nq, lane, p.q_and, p.q_xor);
+  y.init(Qh, cy.qrow, p.Nq, lane, p.q_and, p.q_xor);
 
   WideTile<BN> a, b;
   // Block x's rows come first, so its first masked tile is the wave's.

@@ -51,6 +51,10 @@ WORKLOADS = {
 E4M3_MAX = 448.0
 OUTLIER_RATE = 1e-3
 OUTLIER_GAIN = 20.0
+# Score rise (natural units) between consecutive key ranges of the
+# ``stairs`` recipe: 8 > 8 ln 2, so in base 2 each rise exceeds 8 plus the
+# spread of a 64-key tile maximum.
+STAIR_HEIGHT = 8.0
 
 
 # ---------------------------------------------------------------------------
@@ -139,16 +143,39 @@ def _draw(rng, shape, outliers):
     return x
 
 
-def make(B, H, Nq, Nk, d, dtype, seed, causal=False, outliers=False, scale=None, keep_f32=False):
+def make(B, H, Nq, Nk, d, dtype, seed, causal=False, outliers=False, scale=None, keep_f32=False, kgrow=0.0,
+         stairs=0, outlier_tensors="qkv"):
     """Draw Q, K, V (in that order) from ``numpy.random.default_rng(seed)``
     and encode them as ``dtype``.  For e4m3 each tensor gets descale =
-    fp32(amax / 448) and codes = RNE-saturate(x / descale)."""
+    fp32(amax / 448) and codes = RNE-saturate(x / descale).
+
+    ``outlier_tensors`` names the tensors that get outliers (default all
+    three).
+
+    Two recipes make a row's maximum score arrive many key tiles after its
+    first, so that the running row max of the online softmax rises by large
+    steps during the key loop:
+    * ``kgrow`` > 0 multiplies key row j by 1 + kgrow * j / Nk (in float32,
+      before encoding): scores grow gradually along the key axis;
+    * ``stairs`` = n > 0 sets channel 0 of every query row to 1 and channel 0
+      of key row j to STAIR_HEIGHT * floor((n + 1) j / Nk) / scale, so that
+      the scores of the (i+1)-th of n + 1 equal key ranges are raised by
+      i * STAIR_HEIGHT (natural units) over the first range's, while inside
+      a range they spread as in the plain workload."""
     if dtype not in DTYPES:
         raise ValueError(f"unknown dtype {dtype!r}")
     rng = np.random.default_rng(seed)
-    q32 = _draw(rng, (B, H, Nq, d), outliers)
-    k32 = _draw(rng, (B, H, Nk, d), outliers)
-    v32 = _draw(rng, (B, H, Nk, d), outliers)
+    q32 = _draw(rng, (B, H, Nq, d), outliers and "q" in outlier_tensors)
+    k32 = _draw(rng, (B, H, Nk, d), outliers and "k" in outlier_tensors)
+    v32 = _draw(rng, (B, H, Nk, d), outliers and "v" in outlier_tensors)
+    sc = default_scale(d) if scale is None else np.float32(scale)
+    if kgrow:
+        g = (1.0 + float(kgrow) * np.arange(Nk, dtype=np.float64) / Nk).astype(np.float32)
+        k32 = k32 * g[None, None, :, None]
+    if stairs:
+        step = np.floor((stairs + 1) * np.arange(Nk, dtype=np.float64) / Nk)
+        q32[..., 0] = 1.0
+        k32[..., 0] = (STAIR_HEIGHT * step / float(sc)).astype(np.float32)[None, None, :]
     desc = (np.float32(1.0),) * 3
     if dtype == "f16":
         q, k, v = encode_f16(q32), encode_f16(k32), encode_f16(v32)
@@ -164,7 +191,6 @@ def make(B, H, Nq, Nk, d, dtype, seed, causal=False, outliers=False, scale=None,
             enc.append(encode_e4m3(x.astype(np.float64) / np.float64(ds)))
         q, k, v = enc
         desc = tuple(desc)
-    sc = default_scale(d) if scale is None else np.float32(scale)
     out = Inputs(B=B, H=H, Nq=Nq, Nk=Nk, d=d, causal=bool(causal), dtype=dtype, scale=sc,
                  q=q, k=k, v=v, descale=desc)
     if keep_f32:

@@ -74,7 +74,7 @@ enum {
   ATTN_ERR_DTYPE = -4,    /* unknown dtype code */
   ATTN_ERR_ALIGN = -5,    /* q, k, v, o (x, codes) not 16-byte aligned, or lse (descales)
                              not 4-byte aligned */
-  ATTN_ERR_SCALE = -6,    /* scale or a descale is not finite and > 0 */
+  ATTN_ERR_SCALE = -6,    /* scale is not finite, or a descale is not finite and > 0 */
   ATTN_ERR_LAUNCH = -7,   /* the kernel launch failed */
   ATTN_ERR_ALIAS = -8,    /* an output overlaps an input or another output */
   ATTN_ERR_VARIANT = -9   /* unknown kernel variant, or not built for this d and dtype */
@@ -124,7 +124,9 @@ enum {
  *          Nk * d * element size < 2^31 bytes)
  * d        head dimension: 64, 128 or 256
  * causal   0 = full attention, nonzero = bottom-right causal mask
- * scale    multiplies Q K^T before the softmax (finite, > 0), e.g. 1/sqrt(d)
+ * scale    multiplies Q K^T before the softmax, e.g. 1/sqrt(d); any finite
+ *          value: 0 gives the uniform average of the visible values, a
+ *          negative scale favours the least similar keys
  * dtype    an attn_dtype; ATTN_FP8_E4M3 here means unit descales
  * stream   HIP stream to enqueue on (NULL = default stream)
  *
@@ -139,7 +141,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * FlashAttention-3", section 5).  The real value of each input element is
  * its E4M3 code times that tensor's descale.  Scores accumulate in fp32;
  * the probabilities are rounded to E4M3 for the P V product; O is binary16.
- * Arguments as attn_fwd, plus q_descale, k_descale, v_descale (finite, > 0).
+ * Arguments as attn_fwd, plus q_descale, k_descale, v_descale (finite, > 0);
+ * scale * q_descale * k_descale must be finite.
  */
 int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int Nq, int Nk, int d, int causal, float scale,

@@ -3,24 +3,28 @@ path through the C ABI, decode with the oracle's decoders, and compare
 against the oracle with the stated tolerances.
 
 Tolerances (written here, used by every GPU parity test):
-* fp16 / bf16 inputs: |O_gpu - O_ref| <= 4e-3 + 0.5 * ulp_out(max(|O_ref|, |O_gpu|))
-  per element, and |LSE_gpu - LSE_ref| <= 1e-3.  The half-ulp term is the
-  rounding of the exact result to the output format; it is below 1e-3 for
-  fp16 outputs of magnitude < 4 and only matters for bf16 outputs of
-  magnitude >= 1 (early causal rows average few values of V).
-* fp8 e4m3 inputs: relative RMSE ||O_gpu - O_ref||_F / ||O_ref||_F <= 3e-2
-  over the tensor, O_ref from the oracle on the dequantised inputs.  LSE
-  has no stated fp8 gate; the bound used is derived from the arithmetic:
-  |LSE_gpu - LSE_ref|_i <= 1e-3 + max_j |dS_ij|, where dS is the score error
-  of the E4M3 matrix core.  Its 64-term dot products are not exact in fp32:
-  measured over random E4M3 operands (workload-like, uniform over all
-  codes, small magnitudes) the error of one 32x32x64 product element stayed
-  below 5.1e-4 times the largest |a_k b_k| of that dot product.  With
-  FP8_DOT_EPS = 2^-10 (a 2x margin) and d/64 dot products per score,
-  max_j |dS_ij| <= FP8_DOT_EPS * scale * (d/64) * max_k |q_ik| max_j |k_jk|,
-  and the softmax-weighted LSE error is at most max_j |dS_ij|.
+* binary16 inputs (binary16 O): |O_gpu - O_ref| <= 4e-3 per element, and
+  |LSE_gpu - LSE_ref| <= 1e-3, as stated.
+* bfloat16 inputs (bfloat16 O): |O_gpu - O_ref| <= 4e-3 +
+  0.5 * ulp_bf16(max(|O_ref|, |O_gpu|)), |LSE_gpu - LSE_ref| <= 1e-3.  The
+  half-ulp term is the rounding of the exact result to the output format,
+  which alone exceeds 4e-3 once |O| >= 1 (reading c10).  Where a test passes
+  ``p_abs_v`` (the oracle's P |V| per element: softmax weights applied to
+  the absolute values), the bound adds 2^-9 * (P |V|): the bfloat16 rounding
+  of P that the bfloat16 matrix product requires moves each weight by a
+  relative 2^-9 at most, so O by at most 2^-9 sum_j w_j |v_j|.  On rows
+  spread over many keys these errors cancel; on rows that a few keys
+  dominate they need not, and the rescale tests build such rows on purpose.
+* FP8 E4M3 inputs: relative RMSE ||O_gpu - O_ref||_F / ||O_ref||_F <= 3e-2
+  over the tensor, O_ref from the oracle on the dequantised inputs.  No
+  FP8 LSE gate is stated: |LSE_gpu - LSE_ref| <= 1e-3 (the 16-bit gate) is
+  applied to inputs without outliers; on the 0.1% x20 outlier inputs the
+  E4M3 matrix core's own dot-product rounding grows with the largest
+  products, so there max |dLSE| is reported, not gated.
 """
 
+import concurrent.futures
+import os
 import sys
 
 import numpy as np
@@ -32,16 +36,8 @@ from attention_forward_02_amd import attention
 O_ATOL = 4e-3
 LSE_ATOL = 1e-3
 FP8_REL_RMSE = 3e-2
-FP8_DOT_EPS = 2.0 ** -10
-
-
-def fp8_lse_tol(q, k, scale):
-    """Per-row LSE tolerance for E4M3 inputs (float64 q [B,H,Nq,d], k
-    [B,H,Nk,d], dequantised); see the module docstring."""
-    d = q.shape[-1]
-    colmax = np.abs(k).max(axis=2, keepdims=True)          # [B,H,1,d]
-    m = (np.abs(q) * colmax).max(axis=-1)                  # [B,H,Nq]
-    return LSE_ATOL + FP8_DOT_EPS * scale * (d / 64.0) * m
+BF16_P_EPS = 2.0 ** -9   # bound on the relative rounding error of bfloat16 (RNE)
+LAZY = 8.0               # base-2 rise of a row max beyond which the kernels rescale O and l
 
 
 def say(msg):
@@ -89,6 +85,59 @@ def dequant(inp, heads=None):
     return decode(q, inp.dtype) * qd, decode(k, inp.dtype) * kd, decode(v, inp.dtype) * vd
 
 
+def oracle_all_heads(q, k, v, causal, scale):
+    """oracle.attention over every (b, h) of float64 [B,H,N,d] inputs, one
+    head per task on a thread pool (NumPy releases the GIL in its matrix
+    products and exponentials; each task runs single-threaded BLAS)."""
+    B, H = q.shape[:2]
+    o = np.empty((B, H, q.shape[2], v.shape[3]))
+    lse = np.empty((B, H, q.shape[2]))
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ob, lb = oracle.attention(q[sl], k[sl], v[sl], causal, scale)
+        o[b, h], lse[b, h] = ob[0, 0], lb[0, 0]
+
+    workers = max(1, min(len(os.sched_getaffinity(0)), 16, B * H))
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1, user_api="blas"):
+            with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+                list(ex.map(one, range(B * H)))
+    else:
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, range(B * H)))
+    return o, lse
+
+
+def rescales_from_inputs(q, k, scale, causal, start_tile=0, tile=64):
+    """Per row (float64 q [..., Nq, d], k [..., Nk, d]): how often the lazy
+    online-softmax reference of the kernels is raised after the row's first
+    visible key tile, taking tiles from ``start_tile`` on.  A tile raises it
+    when the tile's row maximum (base 2) exceeds the current reference by
+    more than LAZY; the kernels decide per wave of 32 rows, so a row counted
+    here is sure to have its output and row sum rescaled (by a factor below
+    1, with a nonzero output) at least that often."""
+    Nq, Nk = q.shape[-2], k.shape[-2]
+    s = scale * np.einsum("...id,...jd->...ij", q, k) / np.log(2.0)
+    if causal:
+        allowed = np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq)
+        s = np.where(allowed, s, -np.inf)
+    nt = -(-Nk // tile)
+    m = np.full(s.shape[:-1], -np.inf)
+    count = np.zeros(s.shape[:-1], dtype=np.int64)
+    for t in range(start_tile, nt):
+        tm = s[..., t * tile:(t + 1) * tile].max(axis=-1)
+        up = np.isfinite(m) & (tm > m + LAZY)
+        count += up
+        m = np.where(~np.isfinite(m) | up, np.maximum(m, tm), m)
+    return count
+
+
 def ulp(x, dtype):
     """Spacing of the output format at |x| (float64 array)."""
     man, emin = (10, -14) if dtype == "f16" else (7, -126)
@@ -97,9 +146,11 @@ def ulp(x, dtype):
     return np.exp2(e - man)
 
 
-def compare(o_codes, lse, o_ref, lse_ref, dtype, label="", lse_tol=None):
-    """Assert the tolerances above; return a dict of the observed errors.
-    `lse_tol` (per row, broadcastable to lse) replaces LSE_ATOL when given."""
+def compare(o_codes, lse, o_ref, lse_ref, dtype, label="", lse_gate=True, p_abs_v=None):
+    """Assert the tolerances above; return a dict of the observed errors
+    (max |dO|, the count of elements above 4e-3, max |dLSE|, relative RMSE).
+    ``lse_gate`` False reports E4M3 LSE errors without gating them;
+    ``p_abs_v`` adds the bfloat16 P-rounding term (bf16 only)."""
     od = out_dtype(dtype)
     o = decode(o_codes, od)
     assert np.isfinite(o).all(), f"{label}: non-finite output"
@@ -107,22 +158,27 @@ def compare(o_codes, lse, o_ref, lse_ref, dtype, label="", lse_tol=None):
     assert np.array_equal(np.isfinite(lse), fin), f"{label}: LSE finiteness differs"
     assert np.all(lse[~fin] == -np.inf), f"{label}: empty rows must have LSE = -inf"
     dl = np.abs(lse[fin].astype(np.float64) - lse_ref[fin]) if fin.any() else np.zeros(1)
-    if lse_tol is None:
-        ltol = np.full(dl.shape, LSE_ATOL)
-    else:
-        ltol = np.broadcast_to(lse_tol, lse.shape)[fin] if fin.any() else np.full(1, LSE_ATOL)
     do = np.abs(o - o_ref)
-    stats = dict(max_abs_dO=float(do.max()), n_over_4e3=int((do > O_ATOL).sum()), max_abs_dLSE=float(dl.max()))
+    ref_norm = float(np.sqrt(np.sum(o_ref ** 2)))
+    rel = float(np.sqrt(np.sum(do ** 2)) / ref_norm) if ref_norm > 0 else float(np.sqrt(np.sum(do ** 2)))
+    stats = dict(max_abs_dO=float(do.max()), n_over_4e3=int((do > O_ATOL).sum()), max_abs_dLSE=float(dl.max()),
+                 rel_rmse=rel, n_elements=int(do.size))
     if dtype == "e4m3":
-        rel = float(np.sqrt(np.sum(do ** 2)) / max(np.sqrt(np.sum(o_ref ** 2)), 1e-300))
-        stats["rel_rmse"] = rel
         assert rel <= FP8_REL_RMSE, f"{label}: fp8 relative RMSE {rel:.4g} > {FP8_REL_RMSE}"
     else:
-        tol = O_ATOL + 0.5 * ulp(np.maximum(np.abs(o_ref), np.abs(o)), od)
+        if dtype == "f16":
+            assert p_abs_v is None, "the P-rounding term is a bfloat16 allowance"
+            tol = np.full(do.shape, O_ATOL)
+        else:
+            tol = O_ATOL + 0.5 * ulp(np.maximum(np.abs(o_ref), np.abs(o)), od)
+            if p_abs_v is not None:
+                tol = tol + BF16_P_EPS * p_abs_v
         bad = do > tol
         assert not bad.any(), (f"{label}: {int(bad.sum())} outputs beyond tolerance, worst "
                                f"{float((do - tol).max()):.3g} over; max |dO| {stats['max_abs_dO']:.3g}")
-    bad_l = dl > ltol
-    assert not bad_l.any(), (f"{label}: {int(bad_l.sum())} LSE beyond tolerance; max |dLSE| {dl.max():.3g}, "
-                             f"worst over {float((dl - ltol).max()):.3g}")
+    gated = lse_gate or dtype != "e4m3"
+    stats["lse_gated"] = gated
+    if gated:
+        bad_l = dl > LSE_ATOL
+        assert not bad_l.any(), (f"{label}: {int(bad_l.sum())} LSE beyond tolerance; max |dLSE| {dl.max():.3g}")
     return stats

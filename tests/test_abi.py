@@ -80,7 +80,7 @@ def _call(**kw):
     (dict(dtype=3), b.ATTN_ERR_DTYPE), (dict(dtype=-1), b.ATTN_ERR_DTYPE),
     (dict(q=Q + 8), b.ATTN_ERR_ALIGN), (dict(o=O + 2), b.ATTN_ERR_ALIGN), (dict(lse=L + 2), b.ATTN_ERR_ALIGN),
     (dict(scale=float("nan")), b.ATTN_ERR_SCALE), (dict(scale=float("inf")), b.ATTN_ERR_SCALE),
-    (dict(scale=0.0), b.ATTN_ERR_SCALE), (dict(scale=-0.5), b.ATTN_ERR_SCALE),
+    (dict(scale=float("-inf")), b.ATTN_ERR_SCALE),
     (dict(o=Q), b.ATTN_ERR_ALIAS), (dict(o=Q + 16), b.ATTN_ERR_ALIAS), (dict(lse=V + 4096), b.ATTN_ERR_ALIAS),
     (dict(lse=O + 1024), b.ATTN_ERR_ALIAS),
 ])
@@ -133,7 +133,7 @@ QS, KS, VS = 0x60000000, 0x61000000, 0x62000000
     (dict(q=None), b.ATTN_ERR_NULL), (dict(d=80), b.ATTN_ERR_HEADDIM), (dict(Nk=0), b.ATTN_ERR_SHAPE),
     (dict(qs=QS + 2), b.ATTN_ERR_ALIGN), (dict(vs=VS + 1), b.ATTN_ERR_ALIGN), (dict(q=Q + 4), b.ATTN_ERR_ALIGN),
     (dict(qs=O + 4096), b.ATTN_ERR_ALIAS), (dict(ks=L), b.ATTN_ERR_ALIAS), (dict(o=V), b.ATTN_ERR_ALIAS),
-    (dict(scale=0.0), b.ATTN_ERR_SCALE), (dict(scale=float("nan")), b.ATTN_ERR_SCALE),
+    (dict(scale=float("inf")), b.ATTN_ERR_SCALE), (dict(scale=float("nan")), b.ATTN_ERR_SCALE),
 ])
 def test_blockscaled_validation_rejects_before_launch(kw, code):
     a = dict(q=Q, k=K, v=V, qs=QS, ks=KS, vs=VS, o=O, lse=L, B=1, H=2, Nq=128, Nk=128, d=64, causal=0, scale=0.125)

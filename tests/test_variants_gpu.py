@@ -14,7 +14,7 @@ import oracle
 from attention_forward_02_amd import VARIANT_NAMES, attention, attn_variant_available, inputs
 from attention_forward_02_amd import tune as tuner
 from attention_forward_02_amd.binding import ATTN_BF16, ATTN_F16, ATTN_FP8_E4M3
-from gpu_helpers import compare, dequant, fp8_lse_tol, say, upload
+from gpu_helpers import compare, dequant, oracle_all_heads, say, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -29,8 +29,10 @@ CASES = [(d, dt, var) for d in (64, 128, 256) for dt in ("f16", "bf16", "e4m3") 
 def test_variant_parity(d, dtype, variant, causal, nq, nk):
     label = f"variant {VARIANT_NAMES[variant]} d={d} {dtype} causal={causal} Nq={nq} Nk={nk}"
     say(f"[gpu] {label}: B=2 H=2")
-    inp = inputs.make(2, 2, nq, nk, d, dtype, seed=d + nq + 7 * nk + variant, causal=causal,
-                      outliers=dtype == "e4m3")
+    # E4M3: outliers on the first shape (O gated on relative RMSE, LSE
+    # reported), plain N(0, 1) inputs with the LSE gate on the others
+    outl = dtype == "e4m3" and (nq, nk) == (300, 300)
+    inp = inputs.make(2, 2, nq, nk, d, dtype, seed=d + nq + 7 * nk + variant, causal=causal, outliers=outl)
     q, k, v = (upload(t, dtype) for t in (inp.q, inp.k, inp.v))
     desc = tuple(float(x) for x in inp.descale) if dtype == "e4m3" else None
     o, lse = attention(q, k, v, causal=causal, scale=float(inp.scale), descale=desc, variant=variant)
@@ -38,8 +40,7 @@ def test_variant_parity(d, dtype, variant, causal, nq, nk):
     o_codes = o.view(torch.int16).cpu().numpy().view(np.uint16)
     qq, kk, vv = dequant(inp)
     o_ref, lse_ref = oracle.attention(qq, kk, vv, causal, float(inp.scale))
-    ltol = fp8_lse_tol(qq, kk, float(inp.scale)) if dtype == "e4m3" else None
-    stats = compare(o_codes, lse.cpu().numpy(), o_ref, lse_ref, dtype, label, lse_tol=ltol)
+    stats = compare(o_codes, lse.cpu().numpy(), o_ref, lse_ref, dtype, label, lse_gate=not outl)
     say(f"[gpu] {label}: {stats}")
 
 
@@ -75,23 +76,19 @@ FULL_CASES = [(wl, var) for wl, dt in (("hd128_seq8k_f16", "f16"), ("hd128_seq8k
 
 
 @pytest.mark.parametrize("workload,variant", FULL_CASES, ids=[f"{w}-{VARIANT_NAMES[v]}" for w, v in FULL_CASES])
-def test_variant_full_size_sampled(workload, variant):
+def test_variant_full_size(workload, variant):
     """Every d = 128 variant at the full B=2 H=16 N=8192 size, against the
-    oracle on sampled rows of two heads (the first and the last)."""
+    oracle on every row of two heads (the first and the last)."""
     label = f"variant {VARIANT_NAMES[variant]} {workload}"
-    say(f"[gpu] {label}: B=2 H=16 N=8192 d=128 (sampled)")
+    say(f"[gpu] {label}: B=2 H=16 N=8192 d=128 (heads (0,0), (1,15))")
     inp, q, k, v = _full_workload(workload)
     desc = tuple(float(x) for x in inp.descale) if inp.dtype == "e4m3" else None
     o, lse = attention(q, k, v, causal=False, scale=float(inp.scale), descale=desc, variant=variant)
     torch.cuda.synchronize()
     heads = [(0, 0), (1, 15)]
-    rng = np.random.default_rng(variant)
-    rows = np.unique(np.concatenate([[0, 63, 64, 255, 256, inp.Nq - 1], rng.choice(inp.Nq, 24, replace=False)]))
-    idx = torch.as_tensor(rows, device=o.device)
-    o_sel = np.stack([o[b, h][idx].view(torch.int16).cpu().numpy().view(np.uint16) for b, h in heads])[None]
-    l_sel = np.stack([lse[b, h][idx].cpu().numpy() for b, h in heads])[None]
+    o_sel = np.stack([o[b, h].view(torch.int16).cpu().numpy().view(np.uint16) for b, h in heads])[None]
+    l_sel = np.stack([lse[b, h].cpu().numpy() for b, h in heads])[None]
     qq, kk, vv = dequant(inp, heads)
-    o_ref, lse_ref = oracle.attention(qq, kk, vv, False, float(inp.scale), rows=rows)
-    ltol = fp8_lse_tol(qq, kk, float(inp.scale))[:, :, rows] if inp.dtype == "e4m3" else None
-    stats = compare(o_sel, l_sel, o_ref, lse_ref, inp.dtype, label, lse_tol=ltol)
+    o_ref, lse_ref = oracle_all_heads(qq, kk, vv, False, float(inp.scale))
+    stats = compare(o_sel, l_sel, o_ref, lse_ref, inp.dtype, label, lse_gate=inp.dtype != "e4m3")
     say(f"[gpu] {label}: {stats}")

@@ -5,8 +5,8 @@ the benchmark reports.
     python -m attention_forward_02_amd.profiling OUTDIR WORKLOAD
 
 The first command runs, on one MI355X, a kernel trace of the benchmark
-command (`bench.py --no-cpu --workload WORKLOAD`), four counter passes of a
-short benchmark run, and the FETCH_SIZE / WRITE_SIZE passes of a plain
+command (`bench.py --no-cpu --no-configs --workload WORKLOAD`), five counter
+passes of a short benchmark run (the fifth the L2 hits and misses), and the FETCH_SIZE / WRITE_SIZE passes of a plain
 1 GiB device copy.  The second turns the CSV output into
 `profiles/<kernel>_<WORKLOAD>.md` (the kernel the workload runs) and
 records the calibrated HBM
@@ -52,6 +52,7 @@ PMC_PASSES = [
     ["WRITE_SIZE"],
     ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"],
     ["SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+    ["TCC_HIT_sum", "TCC_MISS_sum"],
 ]
 
 
@@ -145,7 +146,7 @@ def summarize(outdir, workload):
     alg_write = w["B"] * w["H"] * w["Nq"] * (w["d"] * 2 + 4)
     tflops = fl / (avg_ns * 1e-9) / 1e12
     cmd_trace = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {outdir}/trace -o run -- "
-                 f"python3 bench.py --no-cpu --workload {workload}")
+                 f"python3 bench.py --no-cpu --no-configs --workload {workload}")
     lines = [
         f"# {kname} on {workload}",
         "",
@@ -187,7 +188,7 @@ def summarize(outdir, workload):
     ]
     for i, names in enumerate(PMC_PASSES, 1):
         lines.append(f"timeout -s KILL 60 rocprofv3 --pmc {' '.join(names)} --output-format csv -d {outdir}/pmc{i} "
-                     f"-o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu --workload {workload}")
+                     f"-o run -- python3 bench.py --steps 2 --warmup 1 --settle 0 --no-cpu --no-configs --workload {workload}")
     for name in ("FETCH_SIZE", "WRITE_SIZE"):
         lines.append(f"timeout -s KILL 60 rocprofv3 --pmc {name} --output-format csv -d {outdir}/copy_{name} "
                      f"-o run -- python3 bench.py --copy-mib 1024 --steps 2 --warmup 1")
@@ -207,6 +208,8 @@ def summarize(outdir, workload):
         f"| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs)) | {100 * mfma_busy:.1f} % |",
         f"| LDS bank conflict cycles / LDS active cycles | {lds_conf:.4f} |",
         f"| VALU instructions per MFMA | {c['SQ_INSTS_VALU'] / max(1.0, c['SQ_INSTS_MFMA']):.2f} |",
+        f"| L2 hit rate (TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)) | "
+        f"{100 * c['TCC_HIT_sum'] / max(1.0, c['TCC_HIT_sum'] + c['TCC_MISS_sum']):.1f} % |",
         f"| copy calibration FETCH_SIZE (1 GiB read) | {copy['FETCH_SIZE']:.6g} KiB -> factor {f_fetch:.4f} |",
         f"| copy calibration WRITE_SIZE (1 GiB written) | {copy['WRITE_SIZE']:.6g} KiB -> factor {f_write:.4f} |",
         f"| HBM read per launch (calibrated) | {fetch_b / 1e6:.1f} MB |",

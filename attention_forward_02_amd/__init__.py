@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     ATTN_ERR_SCALE,
     ATTN_ERR_SHAPE,
     ATTN_ERR_VARIANT,
+    ATTN_ERR_WORKSPACE,
     ATTN_F16,
     ATTN_FP8_E4M3,
     ATTN_OK,
@@ -35,13 +36,18 @@ from .binding import (  # noqa: F401
     attention,
     attention_fp8_blockscaled,
     attention_fp8_smoothed,
+    attention_splitkv,
     attn_fwd,
     attn_fwd_fp8,
     attn_fwd_fp8_blockscaled,
+    attn_fwd_splitkv,
+    attn_fwd_splitkv_num_splits,
+    attn_fwd_splitkv_workspace_bytes,
     attn_fwd_variant,
     attn_quantize_fp8,
     attn_status_str,
     attn_variant_available,
     load_library,
     quantize_fp8,
+    splitkv_workspace,
 )

@@ -2,12 +2,14 @@
 
 The C functions keep their names: ``attn_fwd``, ``attn_fwd_fp8``,
 ``attn_fwd_variant``, ``attn_variant_available``, ``attn_quantize_fp8``,
-``attn_fwd_fp8_blockscaled`` and ``attn_status_str``
+``attn_fwd_fp8_blockscaled``, ``attn_fwd_splitkv`` (with
+``attn_fwd_splitkv_workspace_bytes`` and ``attn_fwd_splitkv_num_splits``)
+and ``attn_status_str``
 take the same arguments as in include/attn.h, with any pointer given either
 as an integer device address or as a torch tensor (its ``data_ptr()``), and
 the stream as a torch stream, an integer handle or None (the current torch
-stream).  ``attention``, ``quantize_fp8``, ``attention_fp8_blockscaled`` and
-``attention_fp8_smoothed`` are convenience wrappers that allocate the
+stream).  ``attention``, ``attention_splitkv``, ``quantize_fp8``,
+``attention_fp8_blockscaled`` and ``attention_fp8_smoothed`` are convenience wrappers that allocate the
 outputs with torch and raise ``AttnError`` on a non-zero status.  Every step of the computation runs in the HIP library; if the
 library is missing, calls raise instead of falling back to anything else.
 """
@@ -35,6 +37,7 @@ ATTN_ERR_SCALE = -6
 ATTN_ERR_LAUNCH = -7
 ATTN_ERR_ALIAS = -8
 ATTN_ERR_VARIANT = -9
+ATTN_ERR_WORKSPACE = -10
 
 ATTN_VARIANT_AUTO = 0
 ATTN_VARIANT_PIPELINED = 1
@@ -80,6 +83,13 @@ def load_library(path=LIB_PATH):
     lib.attn_quantize_fp8.restype = ci
     lib.attn_fwd_fp8_blockscaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
     lib.attn_fwd_fp8_blockscaled.restype = ci
+    ull = ctypes.c_ulonglong
+    lib.attn_fwd_splitkv_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci, ci]
+    lib.attn_fwd_splitkv_workspace_bytes.restype = ull
+    lib.attn_fwd_splitkv_num_splits.argtypes = [ci, ci, ci, ci, ci, ci, ci]
+    lib.attn_fwd_splitkv_num_splits.restype = ci
+    lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, cf, cf, cf, ci, vp, ull, vp]
+    lib.attn_fwd_splitkv.restype = ci
     lib.attn_status_str.argtypes = [ci]
     lib.attn_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -147,6 +157,28 @@ def attn_fwd_fp8_blockscaled(q, k, v, q_descales, k_descales, v_descales, o, lse
     return lib.attn_fwd_fp8_blockscaled(_ptr(q), _ptr(k), _ptr(v), _ptr(q_descales), _ptr(k_descales),
                                         _ptr(v_descales), _ptr(o), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
                                         int(d), int(bool(causal)), float(scale), _stream(stream))
+
+
+def attn_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, num_splits=0):
+    """The C ``attn_fwd_splitkv_workspace_bytes`` (0 for an unsupported d or dtype)."""
+    return int(load_library().attn_fwd_splitkv_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(d), int(dtype),
+                                                               int(num_splits)))
+
+
+def attn_fwd_splitkv_num_splits(B, H, Nq, Nk, d, dtype, num_splits=0):
+    """The C ``attn_fwd_splitkv_num_splits``."""
+    return int(load_library().attn_fwd_splitkv_num_splits(int(B), int(H), int(Nq), int(Nk), int(d), int(dtype),
+                                                          int(num_splits)))
+
+
+def attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, q_descale, k_descale, v_descale,
+                     num_splits, workspace, workspace_bytes, stream=None):
+    """The C ``attn_fwd_splitkv``; returns its status code."""
+    lib = load_library()
+    return lib.attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
+                                int(d), int(bool(causal)), float(scale), int(dtype), float(q_descale),
+                                float(k_descale), float(v_descale), int(num_splits), _ptr(workspace),
+                                int(workspace_bytes), _stream(stream))
 
 
 def attn_status_str(status):
@@ -236,6 +268,46 @@ def attention(q, k, v, causal=False, scale=None, descale=None, stream=None, vari
         st = attn_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, qd, kd, vd, stream)
     else:
         st = attn_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, code, stream)
+    if st != ATTN_OK:
+        raise AttnError(st)
+    return o, lse
+
+
+def splitkv_workspace(q, k, num_splits=0):
+    """A device workspace (uint8 tensor, possibly empty) for
+    ``attention_splitkv`` on inputs shaped like q and k, reusable by later
+    calls on the same stream."""
+    import torch
+    B, H, Nq, d = q.shape
+    if attn_fwd_splitkv_num_splits(B, H, Nq, k.shape[2], d, _dtype_code(q), num_splits) == 0:
+        raise ValueError("unsupported head dim or dtype")
+    n = attn_fwd_splitkv_workspace_bytes(B, H, Nq, k.shape[2], d, _dtype_code(q), num_splits)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def attention_splitkv(q, k, v, causal=False, scale=None, descale=None, num_splits=0, workspace=None, stream=None):
+    """``attention`` through ``attn_fwd_splitkv``: the key range of every
+    query tile split over up to ``num_splits`` workgroups (0 = the library's
+    choice) and merged.  ``workspace`` is a device tensor from
+    ``splitkv_workspace`` (allocated here when None)."""
+    import torch
+    _check_qkv(q, k, v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = splitkv_workspace(q, k, num_splits)
+    elif not getattr(workspace, "is_cuda", False) or workspace.device != q.device:
+        raise ValueError("workspace must be a tensor on q's device")
+    out_dtype = torch.bfloat16 if code == ATTN_BF16 else torch.float16
+    o = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    qd, kd, vd = descale if (descale is not None and code == ATTN_FP8_E4M3) else (1.0, 1.0, 1.0)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, code, qd, kd, vd, num_splits, workspace,
+                          nbytes, stream)
     if st != ATTN_OK:
         raise AttnError(st)
     return o, lse

@@ -53,6 +53,7 @@ SOURCES = [
     ("attn_fwd_d64_fp8.hip", VGPR_FORM),
     ("attn_fwd_d128_fp8.hip", VGPR_FORM),
     ("attn_fwd_d256_fp8.hip", VGPR_FORM),
+    ("attn_fwd_splitkv.hip", VGPR_FORM),
     ("attn_quant.hip", []),
 ]
 

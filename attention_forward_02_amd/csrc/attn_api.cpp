@@ -65,15 +65,18 @@ bool variant_available(int d, int dtype, int variant) {
   }
 }
 
-int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
-        int causal, float scale, int dtype, float q_ds, float k_ds, float v_ds, int variant, ihipStream_t* stream) {
-  int st = validate(q, k, v, o, lse, B, H, Nq, Nk, d, dtype);
-  if (st != ATTN_OK) return st;
-  if (!variant_available(d, dtype, variant)) return ATTN_ERR_VARIANT;
+// Scale and descales of a per-tensor call: the scale any finite value, the
+// descales finite and > 0, their product finite.
+int check_scales(float scale, float q_ds, float k_ds, float v_ds) {
   if (!isfinite(scale) || !positive_finite(q_ds) || !positive_finite(k_ds) || !positive_finite(v_ds))
     return ATTN_ERR_SCALE;
-  const float s = scale * q_ds * k_ds;
-  if (!isfinite(s)) return ATTN_ERR_SCALE;
+  if (!isfinite(scale * q_ds * k_ds)) return ATTN_ERR_SCALE;
+  return ATTN_OK;
+}
+
+attn::Problem make_problem(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                           int Nk, int d, int causal, float scale, int dtype, float q_ds, float k_ds, float v_ds,
+                           int variant) {
   attn::Problem p;
   p.q = q;
   p.k = k;
@@ -87,11 +90,59 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   p.d = d;
   p.causal = causal != 0;
   p.dtype = dtype;
-  p.scale = s;
+  p.scale = scale * q_ds * k_ds;
   p.v_descale = v_ds;
   p.q_descales = p.k_descales = p.v_descales = nullptr;
   p.variant = variant;
+  p.num_splits = 0;
+  p.workspace = nullptr;
+  p.workspace_bytes = 0;
+  return p;
+}
+
+int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
+        int causal, float scale, int dtype, float q_ds, float k_ds, float v_ds, int variant, ihipStream_t* stream) {
+  int st = validate(q, k, v, o, lse, B, H, Nq, Nk, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!variant_available(d, dtype, variant)) return ATTN_ERR_VARIANT;
+  st = check_scales(scale, q_ds, k_ds, v_ds);
+  if (st != ATTN_OK) return st;
+  const attn::Problem p = make_problem(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, q_ds, k_ds, v_ds,
+                                       variant);
   return attn::launch_forward(p, (hipStream_t)stream);
+}
+
+bool splitkv_args_ok(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits) {
+  return B >= 1 && H >= 1 && Nq >= 1 && Nk >= 1 && num_splits >= 0 && (d == 64 || d == 128 || d == 256) &&
+         (dtype == ATTN_F16 || dtype == ATTN_BF16 || dtype == ATTN_FP8_E4M3);
+}
+
+// The split-key forward on a caller's workspace (attn_fwd_splitkv).
+int run_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                int d, int causal, float scale, int dtype, float q_ds, float k_ds, float v_ds, int num_splits,
+                void* ws, size_t ws_bytes, ihipStream_t* stream) {
+  int st = validate(q, k, v, o, lse, B, H, Nq, Nk, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_FP8_E4M3) q_ds = k_ds = v_ds = 1.f;
+  st = check_scales(scale, q_ds, k_ds, v_ds);
+  if (st != ATTN_OK) return st;
+  if (num_splits < 0) return ATTN_ERR_SHAPE;
+  const size_t need = attn::splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, num_splits);
+  if (need > 0) {
+    if (!ws || !aligned(ws, 256) || ws_bytes < need) return ATTN_ERR_WORKSPACE;
+    const size_t in_elt = dtype == ATTN_FP8_E4M3 ? 1 : 2;
+    const size_t qb = (size_t)B * H * Nq * d * in_elt, kb = (size_t)B * H * Nk * d * in_elt;
+    const size_t ob = (size_t)B * H * Nq * d * 2, lb = (size_t)B * H * Nq * sizeof(float);
+    if (overlap(ws, need, q, qb) || overlap(ws, need, k, kb) || overlap(ws, need, v, kb) ||
+        overlap(ws, need, o, ob) || overlap(ws, need, lse, lb))
+      return ATTN_ERR_WORKSPACE;
+  }
+  attn::Problem p = make_problem(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, q_ds, k_ds, v_ds,
+                                 ATTN_VARIANT_AUTO);
+  p.num_splits = num_splits;
+  p.workspace = ws;
+  p.workspace_bytes = ws_bytes;
+  return attn::launch_splitkv(p, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -180,7 +231,28 @@ int attn_fwd_fp8_blockscaled(const void* q, const void* k, const void* v, const 
   p.k_descales = k_descales;
   p.v_descales = v_descales;
   p.variant = ATTN_VARIANT_AUTO;
+  p.num_splits = 0;
+  p.workspace = nullptr;
+  p.workspace_bytes = 0;
   return attn::launch_forward(p, (hipStream_t)stream);
+}
+
+unsigned long long attn_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype,
+                                                    int num_splits) {
+  if (!splitkv_args_ok(B, H, Nq, Nk, d, dtype, num_splits)) return 0;
+  return attn::splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, num_splits);
+}
+
+int attn_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits) {
+  if (!splitkv_args_ok(B, H, Nq, Nk, d, dtype, num_splits)) return 0;
+  return attn::splitkv_splits(B, H, Nq, Nk, d, dtype, num_splits);
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                     int d, int causal, float scale, int dtype, float q_descale, float k_descale, float v_descale,
+                     int num_splits, void* workspace, unsigned long long workspace_bytes, ihipStream_t* stream) {
+  return run_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, q_descale, k_descale, v_descale,
+                     num_splits, workspace, (size_t)workspace_bytes, stream);
 }
 
 const char* attn_status_str(int status) {
@@ -197,6 +269,9 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case ATTN_ERR_VARIANT: return "unknown kernel variant, or not built for this head dim and dtype";
+    case ATTN_ERR_WORKSPACE:
+      return "split-key workspace is NULL, smaller than the shape needs, not 256-byte aligned or overlapping "
+             "an input or output";
     default: return "unknown status";
   }
 }

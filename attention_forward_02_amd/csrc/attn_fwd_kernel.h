@@ -78,6 +78,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -118,6 +119,10 @@ struct Params {
   const float* ks;
   const float* vs;
   int nqb, nkb;
+  // Split-key forward only (attn_fwd_splitkv.h): partial results, splits
+  // per query tile at most, key tiles per split at most.
+  float* part;
+  int nsplit, split_tiles;
 };
 
 // Input element formats: size and MFMA.

@@ -1,0 +1,74 @@
+// Split-key attention forward (device code in attn_fwd_splitkv.h): every
+// head dimension and input format, causal or not, in one translation unit.
+#include "attn_fwd_splitkv.h"
+
+namespace attn {
+namespace kernels {
+
+#define ATTN_SPLITKV_INSTANCES(D)                                                  \
+  template __global__ void attn_fwd_splitkv_kernel<D, ATTN_F16, false>(Params);    \
+  template __global__ void attn_fwd_splitkv_kernel<D, ATTN_F16, true>(Params);     \
+  template __global__ void attn_fwd_splitkv_kernel<D, ATTN_BF16, false>(Params);   \
+  template __global__ void attn_fwd_splitkv_kernel<D, ATTN_BF16, true>(Params);    \
+  template __global__ void attn_fwd_splitkv_kernel<D, ATTN_FP8_E4M3, false>(Params); \
+  template __global__ void attn_fwd_splitkv_kernel<D, ATTN_FP8_E4M3, true>(Params);      \
+  template __global__ void attn_splitkv_merge_kernel<D, ATTN_F16, false>(Params);  \
+  template __global__ void attn_splitkv_merge_kernel<D, ATTN_F16, true>(Params);   \
+  template __global__ void attn_splitkv_merge_kernel<D, ATTN_BF16, false>(Params); \
+  template __global__ void attn_splitkv_merge_kernel<D, ATTN_BF16, true>(Params);  \
+  template __global__ void attn_splitkv_merge_kernel<D, ATTN_FP8_E4M3, false>(Params); \
+  template __global__ void attn_splitkv_merge_kernel<D, ATTN_FP8_E4M3, true>(Params);
+ATTN_SPLITKV_INSTANCES(64)
+ATTN_SPLITKV_INSTANCES(128)
+ATTN_SPLITKV_INSTANCES(256)
+#undef ATTN_SPLITKV_INSTANCES
+
+template <int D>
+SplitPlan plan_d(int B, int H, int Nq, int Nk, int dtype, int num_splits) {
+  if (dtype == ATTN_FP8_E4M3) return split_plan<D, ATTN_FP8_E4M3>(B, H, Nq, Nk, num_splits);
+  return split_plan<D, ATTN_F16>(B, H, Nq, Nk, num_splits);  // bf16 tiles are the same
+}
+
+SplitPlan plan(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits) {
+  switch (d) {
+    case 64: return plan_d<64>(B, H, Nq, Nk, dtype, num_splits);
+    case 128: return plan_d<128>(B, H, Nq, Nk, dtype, num_splits);
+    default: return plan_d<256>(B, H, Nq, Nk, dtype, num_splits);
+  }
+}
+
+template <int D>
+int launch_d(const Problem& p, hipStream_t s) {
+  switch (p.dtype) {
+    case ATTN_F16:
+      return p.causal ? launch_splitkv_one<D, ATTN_F16, true>(p, s) : launch_splitkv_one<D, ATTN_F16, false>(p, s);
+    case ATTN_BF16:
+      return p.causal ? launch_splitkv_one<D, ATTN_BF16, true>(p, s) : launch_splitkv_one<D, ATTN_BF16, false>(p, s);
+    case ATTN_FP8_E4M3:
+      return p.causal ? launch_splitkv_one<D, ATTN_FP8_E4M3, true>(p, s)
+                      : launch_splitkv_one<D, ATTN_FP8_E4M3, false>(p, s);
+    default:
+      return ATTN_ERR_DTYPE;
+  }
+}
+
+}  // namespace kernels
+
+size_t splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits) {
+  return kernels::plan(B, H, Nq, Nk, d, dtype, num_splits).bytes;
+}
+
+int splitkv_splits(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits) {
+  return kernels::plan(B, H, Nq, Nk, d, dtype, num_splits).nsplit;
+}
+
+int launch_splitkv(const Problem& p, hipStream_t stream) {
+  switch (p.d) {
+    case 64: return kernels::launch_d<64>(p, stream);
+    case 128: return kernels::launch_d<128>(p, stream);
+    case 256: return kernels::launch_d<256>(p, stream);
+    default: return ATTN_ERR_HEADDIM;
+  }
+}
+
+}  // namespace attn

@@ -25,10 +25,21 @@ struct Problem {
   const float* k_descales;
   const float* v_descales;
   int variant;        // ATTN_VARIANT_*; AUTO for attn_fwd / attn_fwd_fp8
+  // Split-key forward (attn_fwd_splitkv) only: splits per query tile (0 =
+  // the library's choice) and the device workspace for partial results.
+  int num_splits;
+  void* workspace;
+  size_t workspace_bytes;
 };
 
 // Launches the forward pass on `stream`.  Returns 0 or a negative ATTN_ERR_*.
 int launch_forward(const Problem& p, hipStream_t stream);
+
+// Split-key forward: workspace bytes a shape needs (0 for an unsupported
+// head dim or dtype), and the launch.
+size_t splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits);
+int splitkv_splits(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits);
+int launch_splitkv(const Problem& p, hipStream_t stream);
 
 // One tensor's block-scaled E4M3 quantisation, validated by the C ABI.
 struct QuantProblem {

@@ -77,7 +77,9 @@ enum {
   ATTN_ERR_SCALE = -6,    /* scale is not finite, or a descale is not finite and > 0 */
   ATTN_ERR_LAUNCH = -7,   /* the kernel launch failed */
   ATTN_ERR_ALIAS = -8,    /* an output overlaps an input or another output */
-  ATTN_ERR_VARIANT = -9   /* unknown kernel variant, or not built for this d and dtype */
+  ATTN_ERR_VARIANT = -9,  /* unknown kernel variant, or not built for this d and dtype */
+  ATTN_ERR_WORKSPACE = -10 /* split-key workspace NULL, smaller than the shape needs, not
+                              256-byte aligned, or overlapping an input or output */
 };
 
 /* Kernel variants (attn_fwd_variant).  All compute the same result; they
@@ -224,6 +226,55 @@ int attn_fwd_fp8_blockscaled(const void* q, const void* k, const void* v,
                              const float* v_descales, void* o, float* lse,
                              int B, int H, int Nq, int Nk, int d, int causal,
                              float scale, struct ihipStream_t* stream);
+
+/*
+ * attn_fwd_splitkv_workspace_bytes: device workspace, in bytes, that
+ * attn_fwd_splitkv needs for this shape and num_splits (0 = the library's
+ * choice): 0 when the shape is not split, and 0 for invalid arguments (use
+ * attn_fwd_splitkv_num_splits to tell them apart).  Host-only.
+ */
+unsigned long long attn_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype,
+                                                    int num_splits);
+
+/*
+ * attn_fwd_splitkv_num_splits: the number of key splits per query tile at
+ * most that attn_fwd_splitkv uses for this shape and num_splits request
+ * (1 = no split), or 0 if d or dtype is not supported.  Host-only.
+ */
+int attn_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits);
+
+/*
+ * attn_fwd_splitkv: the same forward with the key range of each query tile
+ * split over several workgroups, for grids that would not fill the GPU
+ * (few query tiles, long key ranges, the heavy diagonal tiles of a causal
+ * grid).  Each split produces a partial (unnormalised O, row max, row sum)
+ * over its keys, and a second launch on the same stream merges the partials
+ * of a query tile with the online-softmax rescale -- the row max and row sum
+ * the concept card's implementation sketch returns ("Warp specialization",
+ * implementation sketch: output / row_sum and row_max + log(row_sum)) are
+ * exactly what two partial results need to combine.  The merge takes the
+ * splits in a fixed order, so results are bitwise reproducible.
+ *
+ * Arguments as attn_fwd_variant without `variant`, plus:
+ * num_splits       key splits per query tile at most; 0 = the library's
+ *                  choice (enough workgroups to fill the CUs, at least two
+ *                  key tiles per split); 1 = no split (one launch)
+ * workspace        device memory of at least
+ *                  attn_fwd_splitkv_workspace_bytes(...) bytes (0 when the
+ *                  shape is not split; then it may be NULL), 256-byte
+ *                  aligned, owned by the caller, no initial contents needed.
+ *                  Calls that share one workspace must not overlap in time
+ *                  (same stream, or synchronised).
+ * workspace_bytes  its size
+ *
+ * Returns ATTN_ERR_WORKSPACE (before touching the device) for a missing,
+ * misaligned, too small or overlapping workspace, else as attn_fwd.
+ */
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                     int dtype, float q_descale, float k_descale, float v_descale,
+                     int num_splits, void* workspace, unsigned long long workspace_bytes,
+                     struct ihipStream_t* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_str(int status);

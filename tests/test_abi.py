@@ -24,12 +24,14 @@ def _lib():
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", src, flags=re.M)
+    return re.findall(r"^\s*(?:const\s+)?(?:unsigned\s+)?(?:long\s+)*\w+\s*\*?\s*(attn_\w+)\s*\(", src, flags=re.M)
 
 
 def test_header_declares_the_entry_points():
     assert set(_declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_fwd_fp8_blockscaled",
-                                          "attn_variant_available", "attn_fwd_variant", "attn_status_str"}
+                                          "attn_variant_available", "attn_fwd_variant", "attn_fwd_splitkv",
+                                          "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv_num_splits",
+                                          "attn_status_str"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -199,3 +201,72 @@ def test_binding_raises_without_library(tmp_path):
             b.load_library(str(tmp_path / "missing.so"))
     finally:
         b._lib = saved
+
+
+# ---------------------------------------------------------------------------
+# Split-key forward: workspace sizing and validation (host only)
+# ---------------------------------------------------------------------------
+
+def _ws(B, H, Nq, Nk, d, dtype=0, ns=0):
+    return _lib().attn_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, ns)
+
+
+def _nsplit(B, H, Nq, Nk, d, dtype=0, ns=0):
+    return _lib().attn_fwd_splitkv_num_splits(B, H, Nq, Nk, d, dtype, ns)
+
+
+def test_splitkv_plan():
+    # a grid that fills the GPU is not split and needs no workspace
+    assert _nsplit(2, 16, 8192, 8192, 128) == 1 and _ws(2, 16, 8192, 8192, 128) == 0
+    # B=4 H=8 N=1024 d=64: 256 query tiles of 128 rows, one per CU: no split
+    assert _nsplit(4, 8, 1024, 1024, 64) == 1 and _ws(4, 8, 1024, 1024, 64) == 0
+    # B=4 H=8 Nq=128 Nk=1024 d=64: 32 query tiles fill 256 CUs of four
+    # slots with 32 splits, but 16 key tiles allow 8 of at least two tiles
+    assert _nsplit(4, 8, 128, 1024, 64) == 8
+    items, waves, words = 4 * 8, 4, 64 // 32 * 16 + 2
+    assert _ws(4, 8, 128, 1024, 64) == items * 8 * waves * words * 64 * 4
+    # an explicit request splits any grid
+    assert _nsplit(4, 8, 1024, 1024, 64, ns=4) == 4
+    # a single query tile over a long key range splits up to 32 ways, at
+    # least two key tiles each
+    assert _nsplit(1, 1, 100, 1 << 16, 128) == 32
+    assert _nsplit(1, 1, 100, 256, 128) == 2
+    # explicit requests: clamped to the key tiles, rounded to equal tile counts
+    assert _nsplit(1, 1, 64, 640, 64, ns=3) == 3      # 10 tiles -> 4 + 4 + 2
+    assert _nsplit(1, 1, 64, 640, 64, ns=100) == 10
+    assert _nsplit(1, 1, 64, 640, 64, ns=1) == 1
+    # d = 256 16-bit tiles are 32 keys; E4M3 keeps 64
+    assert _nsplit(1, 1, 64, 640, 256, ns=100) == 20
+    assert _nsplit(1, 1, 64, 640, 256, dtype=2, ns=100) == 10
+    # unsupported arguments
+    assert _ws(1, 1, 64, 64, 96) == 0 and _ws(1, 1, 64, 64, 64, dtype=5) == 0 and _ws(0, 1, 64, 64, 64) == 0
+    assert _nsplit(1, 1, 64, 64, 96) == 0 and _nsplit(1, 1, 64, 64, 64, ns=-1) == 0
+
+
+WS = 0x60000000
+
+
+def _splitkv(ws=WS, ws_bytes=None, ns=0, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = _ws(a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["dtype"], max(ns, 0))
+    return _lib().attn_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                                   a["causal"], a["scale"], a["dtype"], 1.0, 1.0, 1.0, ns, ws, ws_bytes, None)
+
+
+# Nk = 4096 over 2 query tiles splits, so every case below needs a workspace
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=None, Nk=4096), b.ATTN_ERR_WORKSPACE), (dict(ws=WS + 64, Nk=4096), b.ATTN_ERR_WORKSPACE),
+    (dict(ws_bytes=1000, Nk=4096), b.ATTN_ERR_WORKSPACE), (dict(ws=Q, Nk=4096), b.ATTN_ERR_WORKSPACE),
+    (dict(ws=O - 4096, Nk=4096), b.ATTN_ERR_WORKSPACE), (dict(ws=L, Nk=4096), b.ATTN_ERR_WORKSPACE),
+    (dict(ns=-1, Nk=4096), b.ATTN_ERR_SHAPE), (dict(d=96, Nk=4096), b.ATTN_ERR_HEADDIM),
+    (dict(q=None, Nk=4096), b.ATTN_ERR_NULL), (dict(scale=float("nan"), Nk=4096), b.ATTN_ERR_SCALE),
+    (dict(dtype=3, Nk=4096), b.ATTN_ERR_DTYPE), (dict(o=Q, Nk=4096), b.ATTN_ERR_ALIAS),
+])
+def test_splitkv_validation_rejects_before_launch(kw, code):
+    a = dict(GOOD)
+    a.update({k: v for k, v in kw.items() if k in a})
+    assert _ws(a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["dtype"], max(kw.get("ns", 0), 0)) > 0 or code not in (
+        b.ATTN_ERR_WORKSPACE,)
+    assert _splitkv(**kw) == code

@@ -1,0 +1,114 @@
+"""GPU parity of the split-key forward (attn_fwd_splitkv) against the oracle.
+
+The key range of each query tile is split over several workgroups whose
+partial results (O, m, l) are merged by the last one to finish with the
+online-softmax rescale.  Covered, through the C ABI:
+* every head dim, input format and causality, with the library's split
+  choice and with forced split counts (two, three, and more splits than the
+  key range has tiles), ragged shapes and Nq != Nk both ways, including
+  causal rows that see no key;
+* the staircase inputs of tests/test_rescale_gpu.py, which give the splits
+  of a query tile row maxima far apart, so the merge weights are far from 1;
+* the B=4 H=8 N=1024 d=64 causal bf16 and B=1 H=1 N=128 d=64 fp16
+  configurations on every element;
+* bitwise-identical repeat calls on one workspace, also after the
+  workspace served another shape in between;
+* scale = 0 and a negative scale.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from attention_forward_02_amd import attention_splitkv, attn_fwd_splitkv_num_splits, inputs, splitkv_workspace
+from attention_forward_02_amd.binding import ATTN_BF16, ATTN_F16, ATTN_FP8_E4M3
+from gpu_helpers import compare, dequant, oracle_all_heads, say, upload
+
+pytestmark = pytest.mark.gpu
+
+CODES = {"f16": ATTN_F16, "bf16": ATTN_BF16, "e4m3": ATTN_FP8_E4M3}
+
+
+def _run(inp, num_splits=0, workspace=None):
+    q, k, v = (upload(t, inp.dtype) for t in (inp.q, inp.k, inp.v))
+    desc = tuple(float(x) for x in inp.descale) if inp.dtype == "e4m3" else None
+    ws = workspace if workspace is not None else splitkv_workspace(q, k, num_splits)
+    o, lse = attention_splitkv(q, k, v, causal=inp.causal, scale=float(inp.scale), descale=desc,
+                               num_splits=num_splits, workspace=ws)
+    torch.cuda.synchronize()
+    return o.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy(), ws
+
+
+def _check(inp, label, num_splits=0, lse_gate=True, p_abs_v=False):
+    ns = attn_fwd_splitkv_num_splits(inp.B, inp.H, inp.Nq, inp.Nk, inp.d, CODES[inp.dtype], num_splits)
+    say(f"[gpu] {label}: B={inp.B} H={inp.H} Nq={inp.Nq} Nk={inp.Nk} d={inp.d} causal={inp.causal} "
+        f"{inp.dtype} requested splits {num_splits} -> {ns}")
+    o, lse, ws = _run(inp, num_splits)
+    q, k, v = dequant(inp)
+    o_ref, lse_ref = oracle_all_heads(q, k, v, inp.causal, float(inp.scale))
+    pav = oracle_all_heads(q, k, np.abs(v), inp.causal, float(inp.scale))[0] if p_abs_v else None
+    stats = compare(o, lse, o_ref, lse_ref, inp.dtype, label, lse_gate=lse_gate, p_abs_v=pav)
+    say(f"[gpu] {label}: {stats}")
+    return o, lse, ws, ns
+
+
+SHAPES = [(300, 300, 3), (129, 1000, 0), (1, 2000, 0), (1000, 127, 2), (64, 4096, 64), (200, 777, 5)]
+
+
+@pytest.mark.parametrize("nq,nk,ns", SHAPES, ids=[f"{a}x{b}-s{c}" for a, b, c in SHAPES])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "e4m3"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_splitkv_parity(d, dtype, causal, nq, nk, ns):
+    inp = inputs.make(1, 2, nq, nk, d, dtype, seed=900 + d + nq + nk + int(causal), causal=causal)
+    _, _, _, used = _check(inp, f"splitkv d{d} {dtype} {'causal' if causal else 'full'} {nq}x{nk}", ns)
+    if ns > 1 or (ns == 0 and nk >= 1000):
+        assert used > 1, "the case was meant to split"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_splitkv_merges_far_apart_maxima(d, dtype):
+    """Staircase scores: each split of a query tile sees a different stair,
+    so partial row maxima differ by steps of 8 and most merge weights are
+    tiny; a wrong weight or a merge in the wrong base misses by far."""
+    inp = inputs.make(1, 2, 256, 1024, d, dtype, seed=31 + d, stairs=3)
+    _check(inp, f"splitkv stairs d{d} {dtype}", num_splits=4)
+
+
+@pytest.mark.parametrize("ns", [0, 4])
+def test_splitkv_causal_d64_bf16_workload(ns):
+    inp = inputs.make_workload("causal_d64_bf16")
+    _check(inp, f"splitkv causal_d64_bf16 (requested splits {ns})", num_splits=ns)
+
+
+def test_splitkv_tiny_d64_f16_workload():
+    inp = inputs.make_workload("tiny_d64_f16")
+    _check(inp, "splitkv tiny_d64_f16 (2 splits)", num_splits=2)
+
+
+def test_splitkv_e4m3_outliers():
+    inp = inputs.make(2, 3, 333, 2000, 128, "e4m3", seed=17, outliers=True)
+    _check(inp, "splitkv e4m3 outliers", lse_gate=False)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1])
+def test_splitkv_nonpositive_scale(scale):
+    inp = inputs.make(1, 2, 200, 1500, 64, "f16", seed=23, causal=True, scale=scale)
+    _check(inp, f"splitkv scale {scale}", num_splits=4)
+
+
+def test_splitkv_repeat_calls_bitwise():
+    inp = inputs.make(2, 4, 300, 3000, 128, "bf16", seed=77, causal=True)
+    o1, l1, ws, ns = _check(inp, "splitkv repeat (first call)")
+    assert ns > 1
+    o2, l2, _ = _run(inp, 0, workspace=ws)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "repeat call differs"
+    # the same workspace for another, smaller shape, then the first again
+    small = inputs.make(1, 2, 100, 700, 128, "bf16", seed=78)
+    q, k, v = dequant(small)
+    o_s, l_s, _ = _run(small, 0, workspace=ws)
+    o_ref, l_ref = oracle_all_heads(q, k, v, False, float(small.scale))
+    compare(o_s, l_s, o_ref, l_ref, "bf16", "splitkv reused workspace")
+    o3, l3, _ = _run(inp, 0, workspace=ws)
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)

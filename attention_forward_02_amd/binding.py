@@ -38,6 +38,8 @@ ATTN_ERR_LAUNCH = -7
 ATTN_ERR_ALIAS = -8
 ATTN_ERR_VARIANT = -9
 ATTN_ERR_WORKSPACE = -10
+ATTN_ERR_SCRATCH = -11
+ATTN_SPLITKV_SCRATCH_BYTES = 64 << 20
 
 ATTN_VARIANT_AUTO = 0
 ATTN_VARIANT_PIPELINED = 1
@@ -90,6 +92,8 @@ def load_library(path=LIB_PATH):
     lib.attn_fwd_splitkv_num_splits.restype = ci
     lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, cf, cf, cf, ci, vp, ull, vp]
     lib.attn_fwd_splitkv.restype = ci
+    lib.attn_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, cf, cf, cf, ci, vp]
+    lib.attn_fwd_splitkv_noalloc.restype = ci
     lib.attn_status_str.argtypes = [ci]
     lib.attn_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -179,6 +183,16 @@ def attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, q_d
                                 int(d), int(bool(causal)), float(scale), int(dtype), float(q_descale),
                                 float(k_descale), float(v_descale), int(num_splits), _ptr(workspace),
                                 int(workspace_bytes), _stream(stream))
+
+
+def attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, q_descale, k_descale,
+                             v_descale, num_splits, stream=None):
+    """The C ``attn_fwd_splitkv_noalloc``; returns its status code."""
+    lib = load_library()
+    return lib.attn_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq),
+                                        int(Nk), int(d), int(bool(causal)), float(scale), int(dtype),
+                                        float(q_descale), float(k_descale), float(v_descale), int(num_splits),
+                                        _stream(stream))
 
 
 def attn_status_str(status):

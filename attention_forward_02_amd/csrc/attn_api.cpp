@@ -255,6 +255,23 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                      num_splits, workspace, (size_t)workspace_bytes, stream);
 }
 
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                             int Nk, int d, int causal, float scale, int dtype, float q_descale, float k_descale,
+                             float v_descale, int num_splits, ihipStream_t* stream) {
+  int st = validate(q, k, v, o, lse, B, H, Nq, Nk, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (num_splits < 0) return ATTN_ERR_SHAPE;
+  const size_t need = attn::splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, num_splits);
+  if (need > (size_t)ATTN_SPLITKV_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = attn::splitkv_scratch(&ws);
+    if (st != ATTN_OK) return st;
+  }
+  return run_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, q_descale, k_descale, v_descale,
+                     num_splits, ws, (size_t)ATTN_SPLITKV_SCRATCH_BYTES, stream);
+}
+
 const char* attn_status_str(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
@@ -269,6 +286,9 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case ATTN_ERR_VARIANT: return "unknown kernel variant, or not built for this head dim and dtype";
+    case ATTN_ERR_SCRATCH:
+      return "the shape needs more than ATTN_SPLITKV_SCRATCH_BYTES of static split-key scratch (use fewer "
+             "splits), or the scratch's device address could not be found";
     case ATTN_ERR_WORKSPACE:
       return "split-key workspace is NULL, smaller than the shape needs, not 256-byte aligned or overlapping "
              "an input or output";

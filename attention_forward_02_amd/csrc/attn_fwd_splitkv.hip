@@ -1,6 +1,15 @@
 // Split-key attention forward (device code in attn_fwd_splitkv.h): every
-// head dimension and input format, causal or not, in one translation unit.
+// head dimension and input format, causal or not, in one translation unit;
+// and the static scratch of its allocation-free entry point.
+#include <mutex>
+
 #include "attn_fwd_splitkv.h"
+
+// Partials of attn_fwd_splitkv_noalloc: one copy per device, held from the
+// library's load until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: every host use goes through the
+// device address looked up by splitkv_scratch() below.
+static __device__ __align__(256) unsigned char scratch[ATTN_SPLITKV_SCRATCH_BYTES];
 
 namespace attn {
 namespace kernels {
@@ -60,6 +69,26 @@ size_t splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, i
 
 int splitkv_splits(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits) {
   return kernels::plan(B, H, Nq, Nk, d, dtype, num_splits).nsplit;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_address[kMaxDevices];  // per device, once looked up
+}  // namespace
+
+int splitkv_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_SCRATCH;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_address[dev]) {
+    // with `dev` current: this device's copy of the array
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return ATTN_ERR_SCRATCH;
+    scratch_address[dev] = a;
+  }
+  *ptr = scratch_address[dev];
+  return ATTN_OK;
 }
 
 int launch_splitkv(const Problem& p, hipStream_t stream) {

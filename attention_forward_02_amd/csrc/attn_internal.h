@@ -40,6 +40,9 @@ int launch_forward(const Problem& p, hipStream_t stream);
 size_t splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits);
 int splitkv_splits(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits);
 int launch_splitkv(const Problem& p, hipStream_t stream);
+// Device address of the current device's static split-key scratch
+// (ATTN_SPLITKV_SCRATCH_BYTES), looked up on the first call per device.
+int splitkv_scratch(void** ptr);
 
 // One tensor's block-scaled E4M3 quantisation, validated by the C ABI.
 struct QuantProblem {

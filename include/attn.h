@@ -78,9 +78,15 @@ enum {
   ATTN_ERR_LAUNCH = -7,   /* the kernel launch failed */
   ATTN_ERR_ALIAS = -8,    /* an output overlaps an input or another output */
   ATTN_ERR_VARIANT = -9,  /* unknown kernel variant, or not built for this d and dtype */
-  ATTN_ERR_WORKSPACE = -10 /* split-key workspace NULL, smaller than the shape needs, not
+  ATTN_ERR_WORKSPACE = -10, /* split-key workspace NULL, smaller than the shape needs, not
                               256-byte aligned, or overlapping an input or output */
+  ATTN_ERR_SCRATCH = -11   /* the shape needs more than ATTN_SPLITKV_SCRATCH_BYTES of static
+                              scratch, or the scratch's device address could not be found */
 };
+
+/* Size of the static device scratch of attn_fwd_splitkv_noalloc (one copy on
+ * every device the library runs on, held until the process ends). */
+#define ATTN_SPLITKV_SCRATCH_BYTES (64u << 20)
 
 /* Kernel variants (attn_fwd_variant).  All compute the same result; they
  * differ in schedule, so their speed depends on the shape:
@@ -275,6 +281,29 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                      int dtype, float q_descale, float k_descale, float v_descale,
                      int num_splits, void* workspace, unsigned long long workspace_bytes,
                      struct ihipStream_t* stream);
+
+/*
+ * attn_fwd_splitkv_noalloc: attn_fwd_splitkv without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The partials live
+ * in a static device array of ATTN_SPLITKV_SCRATCH_BYTES per device; the
+ * call allocates nothing.  Same split plan, kernels and results (bitwise)
+ * as attn_fwd_splitkv with the same num_splits.
+ *
+ * Arguments as attn_fwd_splitkv without workspace and workspace_bytes.  The
+ * current device must be the one `stream` belongs to.
+ *
+ * Every call on one device shares that device's scratch: calls that overlap
+ * in time on one device (different streams, or host threads) race and give
+ * wrong results; serialise them.  Nothing in the scratch needs clearing.
+ * Returns ATTN_ERR_SCRATCH, before touching the device, when the shape needs
+ * more than ATTN_SPLITKV_SCRATCH_BYTES (attn_fwd_splitkv_workspace_bytes
+ * gives the need; a smaller num_splits needs less), else as attn_fwd_splitkv.
+ */
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                             int dtype, float q_descale, float k_descale, float v_descale,
+                             int num_splits, struct ihipStream_t* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_str(int status);

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     assert set(_declared_functions()) == {"attn_fwd", "attn_fwd_fp8", "attn_quantize_fp8", "attn_fwd_fp8_blockscaled",
                                           "attn_variant_available", "attn_fwd_variant", "attn_fwd_splitkv",
                                           "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv_num_splits",
-                                          "attn_status_str"}
+                                          "attn_fwd_splitkv_noalloc", "attn_status_str"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -270,3 +270,19 @@ def test_splitkv_validation_rejects_before_launch(kw, code):
     assert _ws(a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["dtype"], max(kw.get("ns", 0), 0)) > 0 or code not in (
         b.ATTN_ERR_WORKSPACE,)
     assert _splitkv(**kw) == code
+
+
+def test_noalloc_rejects_shapes_beyond_the_static_scratch():
+    # B=1 H=64 Nq=256 Nk=16384 d=128 in 32 splits needs 64 x 32 x 8 waves x
+    # 66 floats x 64 lanes x 4 B = 276 MB of partials, more than the 64 MiB
+    # scratch: rejected before the device is touched
+    need = _ws(1, 64, 256, 16384, 128, 0, 32)
+    assert need == 64 * 32 * 8 * 66 * 64 * 4 > b.ATTN_SPLITKV_SCRATCH_BYTES
+    st = _lib().attn_fwd_splitkv_noalloc(Q, K, V, O, L, 1, 64, 256, 16384, 128, 0, 0.088, 0, 1.0, 1.0, 1.0, 32, None)
+    assert st == b.ATTN_ERR_SCRATCH
+    assert _lib().attn_fwd_splitkv_noalloc(Q, K, V, O, L, 1, 64, 256, 16384, 128, 0, 0.088, 0, 1.0, 1.0, 1.0, -1,
+                                           None) == b.ATTN_ERR_SHAPE
+    assert _lib().attn_fwd_splitkv_noalloc(None, K, V, O, L, 1, 64, 256, 16384, 128, 0, 0.088, 0, 1.0, 1.0, 1.0, 32,
+                                           None) == b.ATTN_ERR_NULL
+    src = open(HEADER).read()
+    assert re.search(r"#define ATTN_SPLITKV_SCRATCH_BYTES \(64u << 20\)", src)

@@ -28,6 +28,8 @@ from .binding import (  # noqa: F401
     ATTN_VARIANT_PIPELINED_4STAGE,
     ATTN_VARIANT_PRODUCER,
     ATTN_VARIANT_SEQUENTIAL,
+    ATTN_VARIANT_SEQUENTIAL_BC32,
+    ATTN_VARIANT_SEQUENTIAL_BC128,
     ATTN_VARIANT_SPLIT,
     ATTN_VARIANT_WIDE,
     VARIANT_NAMES,

@@ -49,6 +49,8 @@ SOURCES = [
     # 64 rows per wave, one wave per SIMD: the default (AGPR) form keeps the
     # output accumulators in AGPRs.
     ("attn_fwd_d128_wide.hip", []),
+    # tile-size variants: the 128-key bf16 kernel spills under the trackers
+    ("attn_fwd_d128_bc.hip", VGPR_FORM),
     ("attn_fwd_d256.hip", VGPR_FORM),
     ("attn_fwd_d64_fp8.hip", VGPR_FORM),
     ("attn_fwd_d128_fp8.hip", VGPR_FORM),

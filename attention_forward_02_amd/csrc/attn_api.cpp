@@ -60,6 +60,10 @@ bool variant_available(int d, int dtype, int variant) {
       return d == 128;
     case ATTN_VARIANT_WIDE:
       return d == 128 && dtype != ATTN_FP8_E4M3;
+    case ATTN_VARIANT_SEQUENTIAL_BC32:
+      return dtype != ATTN_FP8_E4M3 && d != 256;
+    case ATTN_VARIANT_SEQUENTIAL_BC128:
+      return d != 256;
     default:
       return false;
   }

@@ -20,6 +20,10 @@ template __global__ void attn_fwd_kernel<128, ATTN_FP8_E4M3, true, 4>(Params);
 template __global__ void attn_fwd_producer_kernel<128, ATTN_FP8_E4M3, false, 2, 1>(Params);
 template __global__ void attn_fwd_producer_kernel<128, ATTN_FP8_E4M3, true, 2, 1>(Params);
 
+// Key-tile-size variant of the sequential kernel.
+template __global__ void attn_fwd_seq_kernel<128, ATTN_FP8_E4M3, false, false, 128>(Params);
+template __global__ void attn_fwd_seq_kernel<128, ATTN_FP8_E4M3, true, false, 128>(Params);
+
 }  // namespace kernels
 
 int launch_forward_d128_fp8(const Problem& p, hipStream_t stream) { return kernels::launch_fp8<128>(p, stream); }

@@ -25,6 +25,16 @@ template __global__ void attn_fwd_seq_kernel<64, ATTN_F16, true>(Params);
 template __global__ void attn_fwd_seq_kernel<64, ATTN_BF16, false>(Params);
 template __global__ void attn_fwd_seq_kernel<64, ATTN_BF16, true>(Params);
 
+// Key-tile-size variants of the sequential kernel.
+template __global__ void attn_fwd_seq_kernel<64, ATTN_F16, false, false, 32>(Params);
+template __global__ void attn_fwd_seq_kernel<64, ATTN_F16, false, false, 128>(Params);
+template __global__ void attn_fwd_seq_kernel<64, ATTN_F16, true, false, 32>(Params);
+template __global__ void attn_fwd_seq_kernel<64, ATTN_F16, true, false, 128>(Params);
+template __global__ void attn_fwd_seq_kernel<64, ATTN_BF16, false, false, 32>(Params);
+template __global__ void attn_fwd_seq_kernel<64, ATTN_BF16, false, false, 128>(Params);
+template __global__ void attn_fwd_seq_kernel<64, ATTN_BF16, true, false, 32>(Params);
+template __global__ void attn_fwd_seq_kernel<64, ATTN_BF16, true, false, 128>(Params);
+
 }  // namespace kernels
 
 int launch_forward_d64(const Problem& p, hipStream_t stream) { return kernels::launch_16bit<64>(p, stream); }

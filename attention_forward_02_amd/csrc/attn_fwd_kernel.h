@@ -437,8 +437,9 @@ __device__ __forceinline__ void tile_scores(const WaveState8<D>& st, const lds_t
 // O^T += V^T P^T for one tile, V from LDS through transpose reads.  The
 // k-step loop is outermost so that consecutive MFMAs accumulate into
 // different 32-column blocks of O.
-template <int D, int DT, int BN = kBlockN>
-__device__ __forceinline__ void pv_tile(WaveState16<D, DT>& st, const i16x8 (&pf)[4], const lds_t* Vs) {
+template <int D, int DT, int BN = kBlockN, int NPF>
+__device__ __forceinline__ void pv_tile(WaveState16<D, DT>& st, const i16x8 (&pf)[NPF], const lds_t* Vs) {
+  static_assert(BN / 16 <= NPF, "one P fragment per 16 keys");
   constexpr int kRowBytes = D * 2;
 #pragma unroll
   for (int ks = 0; ks < BN / 16; ++ks) {
@@ -527,8 +528,9 @@ __device__ __forceinline__ i16x8 pack8(const f32x16& p, int base) {
 // normalisation consistent with the P V product.  bfloat16's coarser
 // rounding could move LSE by up to 2e-3, so bf16 keeps the fp32 sum of the
 // unrounded p.
-template <int NP>
-__device__ __forceinline__ float row_sum_f16(const i16x8 (&pf)[4]) {
+template <int NP, int NPF>
+__device__ __forceinline__ float row_sum_f16(const i16x8 (&pf)[NPF]) {
+  static_assert(NP <= NPF, "fragments to sum");
   float l[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
@@ -1207,15 +1209,87 @@ __device__ __forceinline__ void seq_step(WaveState<D, DT>& st, const LoopCtxT<BN
   else st.lrun += ls0 + ls1;
 }
 
-// BS: block-scaled E4M3 (per-tile descales, see TileScale).
-template <int D, int DT, bool CAUSAL, bool BS = false>
+// The sequential step over a 128-key tile (the key-tile-size axis of the
+// tuning variants): two 64-key halves share one row max, one reference
+// update and one rescale check, and each barrier hands over twice the keys.
+template <int D, int DT, bool CAUSAL, bool MASKED>
+__device__ __forceinline__ void seq_step128(WaveState<D, DT>& st, const LoopCtxT<128>& cx, int j, const lds_t* Kc,
+                                            const lds_t* Vc) {
+  constexpr int kRowBytes = D * Fmt<DT>::kBytes;
+  constexpr int kHalf = 64 * kRowBytes;
+  f32x16 s0, s1, s2, s3;
+  if constexpr (MASKED) {
+    const int rem = cx.visible(j) ? cx.template mask_rem<CAUSAL>(j) : -(1 << 30);
+    mask_bias<64>(s0, s1, rem);
+    mask_bias<64>(s2, s3, rem - 64);
+    tile_scores<D, DT, true, 64>(st, Kc, s0, s1);
+    tile_scores<D, DT, true, 64>(st, Kc + kHalf, s2, s3);
+  } else {
+    tile_scores<D, DT, false, 64>(st, Kc, s0, s1);
+    tile_scores<D, DT, false, 64>(st, Kc + kHalf, s2, s3);
+  }
+  float ma = fmaxf(s0[0], s1[0]), mb = fmaxf(s2[0], s3[0]);
+#pragma unroll
+  for (int r = 1; r < 16; ++r) {
+    ma = fmaxf(fmaxf(ma, s0[r]), s1[r]);
+    mb = fmaxf(fmaxf(mb, s2[r]), s3[r]);
+  }
+  bool rescale;
+  const float alpha = update_reference(st.m2, swap_halves_max(fmaxf(ma, mb)) * cx.c, rescale);
+  if (rescale) {
+    asm volatile("" ::: "memory");  // keep the branch (see step)
+    st.lrun *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha;
+  }
+  const float mref = (st.m2 == -__builtin_inff()) ? 0.f : st.m2;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cx.c, -mref));
+    s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cx.c, -mref));
+    s2[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], cx.c, -mref));
+    s3[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s3[r], cx.c, -mref));
+  }
+  if constexpr (DT != ATTN_F16) {
+    // row sum of the unrounded p, before the scores die in the packing
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      ls0 += s0[r] + s2[r];
+      ls1 += s1[r] + s3[r];
+    }
+    st.lrun += ls0 + ls1;
+  }
+  if constexpr (DT == ATTN_FP8_E4M3) {
+    pv_tile<D>(st, pack_p_fp8(s0, s1), Vc);
+    pv_tile<D>(st, pack_p_fp8(s2, s3), Vc + kHalf);
+  } else {
+    i16x8 pf[8];
+    pf[0] = pack8<DT>(s0, 0);
+    pf[1] = pack8<DT>(s0, 8);
+    pf[2] = pack8<DT>(s1, 0);
+    pf[3] = pack8<DT>(s1, 8);
+    pf[4] = pack8<DT>(s2, 0);
+    pf[5] = pack8<DT>(s2, 8);
+    pf[6] = pack8<DT>(s3, 0);
+    pf[7] = pack8<DT>(s3, 8);
+    pv_tile<D, DT, 128>(st, pf, Vc);
+    if constexpr (DT == ATTN_F16) st.lrun += row_sum_f16<8>(pf);
+  }
+}
+
+// BS: block-scaled E4M3 (per-tile descales, see TileScale).  BNV: keys per
+// tile, 0 for the default (TileKeys); 32 or 128 for the tile-size variants.
+template <int D, int DT, bool CAUSAL, bool BS = false, int BNV = 0>
 __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) __attribute__((amdgpu_waves_per_eu(2)))
 attn_fwd_seq_kernel(Params p) {
   static_assert(!BS || DT == ATTN_FP8_E4M3, "block scales are an E4M3 variant");
   constexpr int kWaves = Waves<D, DT>::value;
   constexpr int kBlockM = kWaves * kRowsPerWave;
   constexpr int kRowBytes = D * Fmt<DT>::kBytes;
-  constexpr int BN = TileKeys<D, DT>::value;
+  constexpr int BN = BNV ? BNV : TileKeys<D, DT>::value;
+  static_assert(!BS || BN == 64, "block-scaled tiles are one 64-row block");
+  static_assert(DT != ATTN_FP8_E4M3 || BN == 64 || BN == 128, "E4M3 tiles are multiples of the MFMA's 64 keys");
   constexpr int kTileBytes = BN * kRowBytes;
   __shared__ __attribute__((aligned(1024))) unsigned char k_st0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char k_st1[kTileBytes];
@@ -1296,7 +1370,8 @@ attn_fwd_seq_kernel(Params p) {
         vd = vsh[j + 1];
       }
     }
-    seq_step<D, DT, CAUSAL, M, BN, BS>(st, cx, j, Kc, Vc, ts);
+    if constexpr (BN == 128) seq_step128<D, DT, CAUSAL, M>(st, cx, j, Kc, Vc);
+    else seq_step<D, DT, CAUSAL, M, BN, BS>(st, cx, j, Kc, Vc, ts);
   };
   int j = 0;
   for (; j < jm; j += 2) {
@@ -1571,6 +1646,15 @@ struct UseProducer {
   static constexpr bool value = D == 128 && DT == ATTN_F16;
 };
 
+// E4M3 at d = 128 takes the sequential kernel with 128-key tiles: its step
+// is bound by softmax VALU work, and one row max, reference update and
+// barrier per 128 keys instead of per 64 measured 5% faster than 64-key
+// tiles on B=2 H=16 N=8192 with outliers (0.557 vs 0.585 ms).
+template <int D, int DT>
+struct UseBC128 {
+  static constexpr bool value = D == 128 && DT == ATTN_FP8_E4M3;
+};
+
 // Kernel choices a caller can make (include/attn.h, attn_fwd_variant):
 // the pipelined kernel with a two- or four-stage ring (not at d = 256, whose
 // pipelined registers leave one wave per SIMD), the sequential kernel, the
@@ -1584,11 +1668,18 @@ struct Variants {
   static constexpr bool pingpong = D == 128 && DT != ATTN_FP8_E4M3;
   static constexpr bool producer = D == 128;
   static constexpr bool wide = D == 128 && DT != ATTN_FP8_E4M3;
+  // key-tile-size axis of the sequential kernel: 32 keys (16-bit d = 64,
+  // 128; 16-bit d = 256 already runs 32) and 128 keys (d = 64, 128; at
+  // d = 256 the four score accumulators do not fit beside O and Q)
+  static constexpr bool bc32 = DT != ATTN_FP8_E4M3 && D != 256;
+  static constexpr bool bc128 = D != 256;
 };
 
 // The wide-wave kernels (attn_fwd_wide.h) live in a translation unit of
 // their own, built with the compiler's default MFMA register form.
 int launch_wide_d128(const Params& p, int dtype, bool causal, hipStream_t stream);
+// The 16-bit d = 128 tile-size variants likewise (attn_fwd_d128_bc.hip).
+int launch_seq_bc_d128(const Params& p, int dtype, bool causal, int bn, hipStream_t stream);
 
 // Score scaling of a launch.  The kernels need c = scale * log2(e) > 0: the
 // -inf mask bias must stay -inf after the multiply, and the row max must be
@@ -1638,6 +1729,7 @@ int launch_one(const Problem& pr, hipStream_t stream) {
   if (variant == ATTN_VARIANT_AUTO) {
     variant = Sequential<D, DT>::value ? ATTN_VARIANT_SEQUENTIAL : ATTN_VARIANT_PIPELINED;
     if (UseProducer<D, DT>::value) variant = ATTN_VARIANT_PRODUCER;
+    if (UseBC128<D, DT>::value) variant = ATTN_VARIANT_SEQUENTIAL_BC128;
     // Split-key kernel while 128-row query tiles do not fill two rounds of
     // the 256 CUs (and there are enough of them to be worth splitting).
     if (UseSplit<D, DT>::value && grid128 >= kSplitMinGrid && grid128 <= kSplitMaxGrid)
@@ -1684,6 +1776,21 @@ int launch_one(const Problem& pr, hipStream_t stream) {
       return ATTN_ERR_VARIANT;
     case ATTN_VARIANT_WIDE:
       if constexpr (Variants<D, DT>::wide) return launch_wide_d128(p, DT, CAUSAL, stream);
+      return ATTN_ERR_VARIANT;
+    case ATTN_VARIANT_SEQUENTIAL_BC32:
+      if constexpr (Variants<D, DT>::bc32) {
+        if constexpr (D == 128) return launch_seq_bc_d128(p, DT, CAUSAL, 32, stream);
+        else hipLaunchKernelGGL((attn_fwd_seq_kernel<D, DT, CAUSAL, false, 32>), dim3(p.total_tiles), block, 0, stream, p);
+        break;
+      }
+      return ATTN_ERR_VARIANT;
+    case ATTN_VARIANT_SEQUENTIAL_BC128:
+      if constexpr (Variants<D, DT>::bc128) {
+        if constexpr (D == 128 && DT != ATTN_FP8_E4M3) return launch_seq_bc_d128(p, DT, CAUSAL, 128, stream);
+        else hipLaunchKernelGGL((attn_fwd_seq_kernel<D, DT, CAUSAL, false, 128>), dim3(p.total_tiles), block, 0, stream,
+                                p);
+        break;
+      }
       return ATTN_ERR_VARIANT;
     default:
       return ATTN_ERR_VARIANT;

@@ -38,7 +38,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_JSON = os.path.join(PROFILES, "traffic.json")
 
 KERNEL_SOURCES = ["csrc/attn_fwd_kernel.h", "csrc/attn_fwd_wide.h", "csrc/attn_fwd_d64.hip",
-                  "csrc/attn_fwd_d128.hip", "csrc/attn_fwd_d128_wide.hip", "csrc/attn_fwd_d256.hip",
+                  "csrc/attn_fwd_d128.hip", "csrc/attn_fwd_d128_wide.hip", "csrc/attn_fwd_d128_bc.hip", "csrc/attn_fwd_d256.hip",
                   "csrc/attn_fwd_d64_fp8.hip", "csrc/attn_fwd_d128_fp8.hip", "csrc/attn_fwd_d256_fp8.hip",
                   "csrc/attn_quant.hip", "csrc/attn_internal.h", "csrc/attn_fwd_splitkv.h",
                   "csrc/attn_fwd_splitkv.hip", "build.py"]

@@ -37,7 +37,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 VARIANTS = [b.ATTN_VARIANT_AUTO, b.ATTN_VARIANT_PIPELINED, b.ATTN_VARIANT_PIPELINED_4STAGE,
             b.ATTN_VARIANT_SEQUENTIAL, b.ATTN_VARIANT_SPLIT, b.ATTN_VARIANT_PINGPONG,
-            b.ATTN_VARIANT_PRODUCER, b.ATTN_VARIANT_WIDE]
+            b.ATTN_VARIANT_PRODUCER, b.ATTN_VARIANT_WIDE, b.ATTN_VARIANT_SEQUENTIAL_BC32,
+            b.ATTN_VARIANT_SEQUENTIAL_BC128]
 
 
 def _agree(o, lse, o_ref, lse_ref, fp8):

@@ -110,7 +110,11 @@ enum {
  *   WIDE               64 query rows per wave (two 32-row blocks sharing
  *                      every K and V operand read), one wave per SIMD with
  *                      the output accumulators in AGPRs, pipelined steps
- *                      (16-bit d = 128) */
+ *                      (16-bit d = 128)
+ *   SEQUENTIAL_BC32    SEQUENTIAL with 32-key tiles (16-bit d = 64, 128)
+ *   SEQUENTIAL_BC128   SEQUENTIAL with 128-key tiles: one row max,
+ *                      reference update and barrier per 128 keys (d = 64,
+ *                      128) */
 enum {
   ATTN_VARIANT_AUTO = 0,
   ATTN_VARIANT_PIPELINED = 1,
@@ -119,7 +123,9 @@ enum {
   ATTN_VARIANT_SPLIT = 4,
   ATTN_VARIANT_PINGPONG = 5,
   ATTN_VARIANT_PRODUCER = 6,
-  ATTN_VARIANT_WIDE = 7
+  ATTN_VARIANT_WIDE = 7,
+  ATTN_VARIANT_SEQUENTIAL_BC32 = 8,
+  ATTN_VARIANT_SEQUENTIAL_BC128 = 9
 };
 
 /*

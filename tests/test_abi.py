@@ -150,7 +150,8 @@ def test_variant_codes_match_header():
     codes = dict((k, int(v)) for k, v in re.findall(r"(ATTN_VARIANT_\w+)\s*=\s*(\d+)", src))
     assert codes == {"ATTN_VARIANT_AUTO": 0, "ATTN_VARIANT_PIPELINED": 1, "ATTN_VARIANT_PIPELINED_4STAGE": 2,
                      "ATTN_VARIANT_SEQUENTIAL": 3, "ATTN_VARIANT_SPLIT": 4, "ATTN_VARIANT_PINGPONG": 5,
-                     "ATTN_VARIANT_PRODUCER": 6, "ATTN_VARIANT_WIDE": 7}
+                     "ATTN_VARIANT_PRODUCER": 6, "ATTN_VARIANT_WIDE": 7, "ATTN_VARIANT_SEQUENTIAL_BC32": 8,
+                     "ATTN_VARIANT_SEQUENTIAL_BC128": 9}
     for name, val in codes.items():
         assert getattr(b, name) == val
 
@@ -159,7 +160,7 @@ def test_variant_availability_table():
     lib = _lib()
     for d in (64, 128, 256):
         for dt in (b.ATTN_F16, b.ATTN_BF16, b.ATTN_FP8_E4M3):
-            got = {v for v in range(-1, 9) if lib.attn_variant_available(d, dt, v)}
+            got = {v for v in range(-1, 16) if lib.attn_variant_available(d, dt, v)}
             want = {b.ATTN_VARIANT_AUTO, b.ATTN_VARIANT_SEQUENTIAL}
             if d != 256:
                 want |= {b.ATTN_VARIANT_PIPELINED, b.ATTN_VARIANT_PIPELINED_4STAGE}
@@ -171,6 +172,10 @@ def test_variant_availability_table():
                 want.add(b.ATTN_VARIANT_PRODUCER)
             if d == 128 and dt != b.ATTN_FP8_E4M3:
                 want.add(b.ATTN_VARIANT_WIDE)
+            if d != 256 and dt != b.ATTN_FP8_E4M3:
+                want.add(b.ATTN_VARIANT_SEQUENTIAL_BC32)
+            if d != 256:
+                want.add(b.ATTN_VARIANT_SEQUENTIAL_BC128)
             assert got == want, (d, dt, got)
     assert not lib.attn_variant_available(96, b.ATTN_F16, 0) and not lib.attn_variant_available(64, 5, 0)
 
@@ -181,7 +186,9 @@ def test_variant_availability_table():
     (dict(dtype=2, variant=4), b.ATTN_ERR_VARIANT), (dict(d=128, variant=4), b.ATTN_ERR_VARIANT),
     (dict(variant=5), b.ATTN_ERR_VARIANT), (dict(d=128, dtype=2, variant=5), b.ATTN_ERR_VARIANT),
     (dict(variant=6), b.ATTN_ERR_VARIANT), (dict(variant=7), b.ATTN_ERR_VARIANT),
-    (dict(d=128, dtype=2, variant=7), b.ATTN_ERR_VARIANT), (dict(d=128, variant=8), b.ATTN_ERR_VARIANT),
+    (dict(d=128, dtype=2, variant=7), b.ATTN_ERR_VARIANT), (dict(d=128, variant=15), b.ATTN_ERR_VARIANT),
+    (dict(dtype=2, variant=8), b.ATTN_ERR_VARIANT), (dict(d=256, variant=8), b.ATTN_ERR_VARIANT),
+    (dict(d=256, variant=9), b.ATTN_ERR_VARIANT), (dict(d=256, dtype=2, variant=9), b.ATTN_ERR_VARIANT),
     (dict(q=None, variant=1), b.ATTN_ERR_NULL), (dict(d=80, variant=1), b.ATTN_ERR_HEADDIM),
     (dict(dtype=2, kd=0.0), b.ATTN_ERR_SCALE), (dict(lse=O + 64), b.ATTN_ERR_ALIAS),
 ])

@@ -36,7 +36,7 @@ from gpu_helpers import compare, dequant, oracle_all_heads, rescales_from_inputs
 pytestmark = pytest.mark.gpu
 
 CODES = {"f16": ATTN_F16, "bf16": ATTN_BF16}
-KERNELS = [(d, dt, var) for d in (64, 128, 256) for dt in ("f16", "bf16") for var in range(8)
+KERNELS = [(d, dt, var) for d in (64, 128, 256) for dt in ("f16", "bf16") for var in range(len(VARIANT_NAMES))
            if attn_variant_available(d, CODES[dt], var)]
 RECIPES = {
     "stairs": dict(stairs=3),

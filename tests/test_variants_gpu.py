@@ -19,7 +19,7 @@ from gpu_helpers import compare, dequant, oracle_all_heads, say, upload
 pytestmark = pytest.mark.gpu
 
 CODES = {"f16": ATTN_F16, "bf16": ATTN_BF16, "e4m3": ATTN_FP8_E4M3}
-CASES = [(d, dt, var) for d in (64, 128, 256) for dt in ("f16", "bf16", "e4m3") for var in (1, 2, 3, 4, 5, 6, 7)
+CASES = [(d, dt, var) for d in (64, 128, 256) for dt in ("f16", "bf16", "e4m3") for var in range(1, len(VARIANT_NAMES))
          if attn_variant_available(d, CODES[dt], var)]
 
 
@@ -50,7 +50,8 @@ def test_tuner_times_every_variant():
     q, k, v = (upload(t, "bf16") for t in (inp.q, inp.k, inp.v))
     rows = tuner.tune(q, k, v, True, float(inp.scale), reps=3, rounds=2, settle_s=0.05)
     names = [r["name"] for r in rows]
-    assert names[0] == "auto" and set(names) == {"auto", "pipelined", "pipelined_4stage", "sequential", "split"}
+    assert names[0] == "auto" and set(names) == {"auto", "pipelined", "pipelined_4stage", "sequential", "split",
+                                                 "sequential_bc32", "sequential_bc128"}
     for r in rows:
         assert r["ms"] is not None and r["ms"] > 0, r
     timed = [r["ms"] for r in rows[1:]]
@@ -72,7 +73,7 @@ def _full_workload(name):
 
 
 FULL_CASES = [(wl, var) for wl, dt in (("hd128_seq8k_f16", "f16"), ("hd128_seq8k_e4m3", "e4m3"))
-              for var in (1, 2, 3, 4, 5, 6, 7) if attn_variant_available(128, CODES[dt], var)]
+              for var in range(1, len(VARIANT_NAMES)) if attn_variant_available(128, CODES[dt], var)]
 
 
 @pytest.mark.parametrize("workload,variant", FULL_CASES, ids=[f"{w}-{VARIANT_NAMES[v]}" for w, v in FULL_CASES])

@@ -74,6 +74,13 @@ def load_library(path=LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built: run `python -m attention_forward_02_amd.build`")
+    # torch ships a HIP runtime of its own: when torch is present it must be
+    # the process's runtime before the library's dependency is resolved, or
+    # tensors allocated by one runtime would reach kernels launched by another
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp]

@@ -1153,60 +1153,151 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) a
 // would leave one wave per SIMD (d = 256).  K_j and V_j share a ring stage;
 // the loads of tile j + 1 are issued at the start of step j.
 // ---------------------------------------------------------------------------
-template <int D, int DT, bool CAUSAL, bool MASKED, int BN, bool BS>
+// Largest half-row sum of probabilities a tile may reach against the current
+// reference before the reference is raised: 2^kLazy, so every p <= 2^kLazy.
+constexpr float kLazySum = 256.0f;
+
+// SUMCHECK (the default for 16-bit inputs below d = 256): the reference is
+// checked through the half-row sums, below.  Without it every tile's row
+// max is taken first, as in step().  Measured against that form on the
+// sequential kernel: binary16 d = 128 +3.8%, bfloat16 d = 64 causal +5%, but
+// E4M3 d = 128 -19% (its row sum is 32 fp32 adds, which the check moves
+// from under the P V product to before it).  The producer-wave kernel and
+// d = 256 keep the max-first form too: holding the packed probabilities
+// through the check does not fit their registers (168 with a producer wave
+// beside two consumers per SIMD; 256 beside O and Q at d = 256).
+template <int D, int DT, bool CAUSAL, bool MASKED, int BN, bool BS,
+          bool SUMCHECK = (D != 256 && DT != ATTN_FP8_E4M3)>
 __device__ __forceinline__ void seq_step(WaveState<D, DT>& st, const LoopCtxT<BN>& cx, int j, const lds_t* Kc,
                                          const lds_t* Vc, const TileScale& ts) {
   f32x16 s0, s1;
   masked_scores<D, DT, CAUSAL, MASKED>(st, cx, j, Kc, s0, s1);
   const float c = BS ? ts.c : cx.c;
-  float m2t = tile_max2<BN>(s0, s1, c);
-  if constexpr (BS) m2t += ts.lv;
-  bool rescale;
-  const float alpha = update_reference(st.m2, m2t, rescale);
-  if (rescale) {
-    asm volatile("" ::: "memory");  // keep the branch (see step)
+  if constexpr (!SUMCHECK) {
+    float m2t = tile_max2<BN>(s0, s1, c);
+    if constexpr (BS) m2t += ts.lv;
+    bool rescale;
+    const float alpha = update_reference(st.m2, m2t, rescale);
+    if (rescale) {
+      asm volatile("" ::: "memory");  // keep the branch (see step)
+      st.lrun *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha;
+    }
+    const float mref = (st.m2 == -__builtin_inff()) ? 0.f : st.m2;
+    const float off = BS ? ts.lv - mref : -mref;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, off));
+      if constexpr (BN == 64) s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, off));
+    }
+    if constexpr (DT == ATTN_FP8_E4M3) {
+      pv_tile<D>(st, pack_p_fp8(s0, s1), Vc);
+    } else {
+      i16x8 pf[4];
+      pf[0] = pack8<DT>(s0, 0);
+      pf[1] = pack8<DT>(s0, 8);
+      if constexpr (BN == 64) {
+        pf[2] = pack8<DT>(s1, 0);
+        pf[3] = pack8<DT>(s1, 8);
+      }
+      pv_tile<D, DT, BN>(st, pf, Vc);
+      if constexpr (DT == ATTN_F16) {
+        st.lrun += row_sum_f16<BN / 16>(pf);
+        return;
+      }
+    }
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      ls0 += s0[r];
+      ls1 += s0[r + 1];
+    }
+    if constexpr (BN == 64) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        ls0 += s1[r];
+        ls1 += s1[r + 1];
+      }
+    }
+    if constexpr (BS) st.lrun = __builtin_fmaf(ls0 + ls1, ts.iv, st.lrun);
+    else st.lrun += ls0 + ls1;
+    return;
+  }
+  i16x8 pf[4];
+  i32x8 pf8;
+  // p = 2^(c s + lv - mref) in place of the scores, packed for the P V
+  // product; returns this lane's half-row sum (of the rounded binary16 P,
+  // else of the unrounded p).
+  auto probs = [&](float mref) -> float {
+    const float off = BS ? ts.lv - mref : -mref;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, off));
+      if constexpr (BN == 64) s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, off));
+    }
+    if constexpr (DT == ATTN_FP8_E4M3) {
+      pf8 = pack_p_fp8(s0, s1);
+    } else {
+      pf[0] = pack8<DT>(s0, 0);
+      pf[1] = pack8<DT>(s0, 8);
+      if constexpr (BN == 64) {
+        pf[2] = pack8<DT>(s1, 0);
+        pf[3] = pack8<DT>(s1, 8);
+      }
+    }
+    if constexpr (DT == ATTN_F16) {
+      return row_sum_f16<BN / 16>(pf);
+    } else {
+      float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        ls0 += s0[r];
+        ls1 += s0[r + 1];
+      }
+      if constexpr (BN == 64) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          ls0 += s1[r];
+          ls1 += s1[r + 1];
+        }
+      }
+      return ls0 + ls1;
+    }
+  };
+  // The reference m2 moves only when it must (lazy rescale).  With a set
+  // reference the probabilities are formed against it directly, and the
+  // half-row sums show whether every p stayed within 2^kLazy; only if one
+  // did not (or a row has no reference yet) is the tile scored again, its
+  // row max taken, the reference raised to it, O and l rescaled by
+  // 2^(old - new), and the probabilities formed again.  The result does
+  // not depend on the reference, only its rounding does.
+  float ls;
+  bool refresh = __any(st.m2 == -__builtin_inff());  // wave-uniform
+  if (!refresh) {
+    ls = probs(st.m2);
+    refresh = __any(!(ls <= kLazySum));
+    if (refresh) {
+      asm volatile("" ::: "memory");  // a real, rarely taken branch
+      masked_scores<D, DT, CAUSAL, MASKED>(st, cx, j, Kc, s0, s1);
+    }
+  }
+  if (refresh) {
+    asm volatile("" ::: "memory");
+    float m2t = tile_max2<BN>(s0, s1, c);
+    if constexpr (BS) m2t += ts.lv;
+    const float m2new = fmaxf(st.m2, m2t);
+    const float alpha = m2new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(st.m2 - m2new);
+    st.m2 = m2new;
     st.lrun *= alpha;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha;
+    ls = probs(m2new == -__builtin_inff() ? 0.f : m2new);
   }
-  const float mref = (st.m2 == -__builtin_inff()) ? 0.f : st.m2;
-  const float off = BS ? ts.lv - mref : -mref;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c, off));
-    if constexpr (BN == 64) s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c, off));
-  }
-  if constexpr (DT == ATTN_FP8_E4M3) {
-    pv_tile<D>(st, pack_p_fp8(s0, s1), Vc);
-  } else {
-    i16x8 pf[4];
-    pf[0] = pack8<DT>(s0, 0);
-    pf[1] = pack8<DT>(s0, 8);
-    if constexpr (BN == 64) {
-      pf[2] = pack8<DT>(s1, 0);
-      pf[3] = pack8<DT>(s1, 8);
-    }
-    pv_tile<D, DT, BN>(st, pf, Vc);
-    if constexpr (DT == ATTN_F16) {
-      st.lrun += row_sum_f16<BN / 16>(pf);
-      return;
-    }
-  }
-  float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; r += 2) {
-    ls0 += s0[r];
-    ls1 += s0[r + 1];
-  }
-  if constexpr (BN == 64) {
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      ls0 += s1[r];
-      ls1 += s1[r + 1];
-    }
-  }
-  if constexpr (BS) st.lrun = __builtin_fmaf(ls0 + ls1, ts.iv, st.lrun);
-  else st.lrun += ls0 + ls1;
+  if constexpr (DT == ATTN_FP8_E4M3) pv_tile<D>(st, pf8, Vc);
+  else pv_tile<D, DT, BN>(st, pf, Vc);
+  if constexpr (BS) st.lrun = __builtin_fmaf(ls, ts.iv, st.lrun);
+  else st.lrun += ls;
 }
 
 // The sequential step over a 128-key tile (the key-tile-size axis of the
@@ -1217,65 +1308,113 @@ __device__ __forceinline__ void seq_step128(WaveState<D, DT>& st, const LoopCtxT
                                             const lds_t* Vc) {
   constexpr int kRowBytes = D * Fmt<DT>::kBytes;
   constexpr int kHalf = 64 * kRowBytes;
+  // The half-row-sum check of seq_step would keep all eight packed P
+  // fragments live through it: 124-392 bytes of spills at 16-bit d = 128.
+  // So the 128-key step takes the row max first.
+  constexpr bool kSumCheck = false;
   f32x16 s0, s1, s2, s3;
-  if constexpr (MASKED) {
-    const int rem = cx.visible(j) ? cx.template mask_rem<CAUSAL>(j) : -(1 << 30);
-    mask_bias<64>(s0, s1, rem);
-    mask_bias<64>(s2, s3, rem - 64);
-    tile_scores<D, DT, true, 64>(st, Kc, s0, s1);
-    tile_scores<D, DT, true, 64>(st, Kc + kHalf, s2, s3);
-  } else {
-    tile_scores<D, DT, false, 64>(st, Kc, s0, s1);
-    tile_scores<D, DT, false, 64>(st, Kc + kHalf, s2, s3);
-  }
-  float ma = fmaxf(s0[0], s1[0]), mb = fmaxf(s2[0], s3[0]);
+  auto scores = [&]() {
+    if constexpr (MASKED) {
+      const int rem = cx.visible(j) ? cx.template mask_rem<CAUSAL>(j) : -(1 << 30);
+      mask_bias<64>(s0, s1, rem);
+      mask_bias<64>(s2, s3, rem - 64);
+      tile_scores<D, DT, true, 64>(st, Kc, s0, s1);
+      tile_scores<D, DT, true, 64>(st, Kc + kHalf, s2, s3);
+    } else {
+      tile_scores<D, DT, false, 64>(st, Kc, s0, s1);
+      tile_scores<D, DT, false, 64>(st, Kc + kHalf, s2, s3);
+    }
+  };
+  i16x8 pf[8];
+  // p in place of the scores, packed (16-bit); returns this lane's half-row
+  // sum (binary16: of the rounded P; else of the unrounded p)
+  auto probs = [&](float mref) -> float {
 #pragma unroll
-  for (int r = 1; r < 16; ++r) {
-    ma = fmaxf(fmaxf(ma, s0[r]), s1[r]);
-    mb = fmaxf(fmaxf(mb, s2[r]), s3[r]);
-  }
-  bool rescale;
-  const float alpha = update_reference(st.m2, swap_halves_max(fmaxf(ma, mb)) * cx.c, rescale);
-  if (rescale) {
-    asm volatile("" ::: "memory");  // keep the branch (see step)
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cx.c, -mref));
+      s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cx.c, -mref));
+      s2[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], cx.c, -mref));
+      s3[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s3[r], cx.c, -mref));
+    }
+    if constexpr (DT != ATTN_FP8_E4M3) {
+      pf[0] = pack8<DT>(s0, 0);
+      pf[1] = pack8<DT>(s0, 8);
+      pf[2] = pack8<DT>(s1, 0);
+      pf[3] = pack8<DT>(s1, 8);
+      pf[4] = pack8<DT>(s2, 0);
+      pf[5] = pack8<DT>(s2, 8);
+      pf[6] = pack8<DT>(s3, 0);
+      pf[7] = pack8<DT>(s3, 8);
+    }
+    if constexpr (DT == ATTN_F16) {
+      return row_sum_f16<8>(pf);
+    } else {
+      float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        ls0 += s0[r] + s2[r];
+        ls1 += s1[r] + s3[r];
+      }
+      return ls0 + ls1;
+    }
+  };
+  // the reference, as in seq_step
+  auto refresh_reference = [&]() {
+    float ma = fmaxf(s0[0], s1[0]), mb = fmaxf(s2[0], s3[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      ma = fmaxf(fmaxf(ma, s0[r]), s1[r]);
+      mb = fmaxf(fmaxf(mb, s2[r]), s3[r]);
+    }
+    const float m2t = swap_halves_max(fmaxf(ma, mb)) * cx.c;
+    const float m2new = fmaxf(st.m2, m2t);
+    const float alpha = m2new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(st.m2 - m2new);
+    st.m2 = m2new;
     st.lrun *= alpha;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha;
-  }
-  const float mref = (st.m2 == -__builtin_inff()) ? 0.f : st.m2;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cx.c, -mref));
-    s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cx.c, -mref));
-    s2[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], cx.c, -mref));
-    s3[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s3[r], cx.c, -mref));
-  }
-  if constexpr (DT != ATTN_F16) {
-    // row sum of the unrounded p, before the scores die in the packing
-    float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      ls0 += s0[r] + s2[r];
-      ls1 += s1[r] + s3[r];
+  };
+  scores();
+  float ls;
+  if constexpr (kSumCheck) {
+    bool refresh = __any(st.m2 == -__builtin_inff());
+    if (!refresh) {
+      ls = probs(st.m2);
+      refresh = __any(!(ls <= kLazySum));
+      if (refresh) {
+        asm volatile("" ::: "memory");  // a real, rarely taken branch
+        scores();
+      }
     }
-    st.lrun += ls0 + ls1;
+    if (refresh) {
+      asm volatile("" ::: "memory");
+      refresh_reference();
+      ls = probs(st.m2 == -__builtin_inff() ? 0.f : st.m2);
+    }
+  } else {
+    float ma = fmaxf(s0[0], s1[0]), mb = fmaxf(s2[0], s3[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      ma = fmaxf(fmaxf(ma, s0[r]), s1[r]);
+      mb = fmaxf(fmaxf(mb, s2[r]), s3[r]);
+    }
+    bool rescale;
+    const float alpha = update_reference(st.m2, swap_halves_max(fmaxf(ma, mb)) * cx.c, rescale);
+    if (rescale) {
+      asm volatile("" ::: "memory");  // keep the branch (see step)
+      st.lrun *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha;
+    }
+    ls = probs(st.m2 == -__builtin_inff() ? 0.f : st.m2);
   }
   if constexpr (DT == ATTN_FP8_E4M3) {
     pv_tile<D>(st, pack_p_fp8(s0, s1), Vc);
     pv_tile<D>(st, pack_p_fp8(s2, s3), Vc + kHalf);
   } else {
-    i16x8 pf[8];
-    pf[0] = pack8<DT>(s0, 0);
-    pf[1] = pack8<DT>(s0, 8);
-    pf[2] = pack8<DT>(s1, 0);
-    pf[3] = pack8<DT>(s1, 8);
-    pf[4] = pack8<DT>(s2, 0);
-    pf[5] = pack8<DT>(s2, 8);
-    pf[6] = pack8<DT>(s3, 0);
-    pf[7] = pack8<DT>(s3, 8);
     pv_tile<D, DT, 128>(st, pf, Vc);
-    if constexpr (DT == ATTN_F16) st.lrun += row_sum_f16<8>(pf);
   }
+  st.lrun += ls;
 }
 
 // BS: block-scaled E4M3 (per-tile descales, see TileScale).  BNV: keys per
@@ -1467,7 +1606,7 @@ __global__ void __launch_bounds__(64 * (8 + NP)) attn_fwd_producer_kernel(Params
   auto step = [&](int j, int s, auto masked) {
     constexpr bool M = decltype(masked)::value;
     __syncthreads();
-    seq_step<D, DT, CAUSAL, M, BN, false>(st, cx, j, (const lds_t*)k_st[s], (const lds_t*)v_st[s], ts);
+    seq_step<D, DT, CAUSAL, M, BN, false, false>(st, cx, j, (const lds_t*)k_st[s], (const lds_t*)v_st[s], ts);
   };
   // Steps run in groups of NS so that each one's stage is a constant.
   const int jm = tb - tb % NS;

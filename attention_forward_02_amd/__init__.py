@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     ATTN_VARIANT_PIPELINED,
     ATTN_VARIANT_PINGPONG,
     ATTN_VARIANT_PIPELINED_4STAGE,
+    ATTN_VARIANT_PIPELINED_3STAGE,
     ATTN_VARIANT_PRODUCER,
     ATTN_VARIANT_SEQUENTIAL,
     ATTN_VARIANT_SEQUENTIAL_BC32,

@@ -51,11 +51,13 @@ ATTN_VARIANT_PRODUCER = 6
 ATTN_VARIANT_WIDE = 7
 ATTN_VARIANT_SEQUENTIAL_BC32 = 8
 ATTN_VARIANT_SEQUENTIAL_BC128 = 9
+ATTN_VARIANT_PIPELINED_3STAGE = 10
 VARIANT_NAMES = {ATTN_VARIANT_AUTO: "auto", ATTN_VARIANT_PIPELINED: "pipelined",
                  ATTN_VARIANT_PIPELINED_4STAGE: "pipelined_4stage", ATTN_VARIANT_SEQUENTIAL: "sequential",
                  ATTN_VARIANT_SPLIT: "split", ATTN_VARIANT_PINGPONG: "pingpong",
                  ATTN_VARIANT_PRODUCER: "producer", ATTN_VARIANT_WIDE: "wide",
-                 ATTN_VARIANT_SEQUENTIAL_BC32: "sequential_bc32", ATTN_VARIANT_SEQUENTIAL_BC128: "sequential_bc128"}
+                 ATTN_VARIANT_SEQUENTIAL_BC32: "sequential_bc32", ATTN_VARIANT_SEQUENTIAL_BC128: "sequential_bc128",
+                 ATTN_VARIANT_PIPELINED_3STAGE: "pipelined_3stage"}
 
 
 class AttnError(RuntimeError):

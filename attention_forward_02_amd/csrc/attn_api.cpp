@@ -64,6 +64,8 @@ bool variant_available(int d, int dtype, int variant) {
       return dtype != ATTN_FP8_E4M3 && d != 256;
     case ATTN_VARIANT_SEQUENTIAL_BC128:
       return d != 256;
+    case ATTN_VARIANT_PIPELINED_3STAGE:
+      return dtype != ATTN_FP8_E4M3 && d != 256;
     default:
       return false;
   }

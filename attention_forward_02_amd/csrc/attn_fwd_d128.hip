@@ -31,6 +31,12 @@ template __global__ void attn_fwd_producer_kernel<128, ATTN_F16, true, 2, 1>(Par
 template __global__ void attn_fwd_producer_kernel<128, ATTN_BF16, false, 2, 1>(Params);
 template __global__ void attn_fwd_producer_kernel<128, ATTN_BF16, true, 2, 1>(Params);
 
+// Three-stage pipelined variant.
+template __global__ void attn_fwd_pipe3_kernel<128, ATTN_F16, false>(Params);
+template __global__ void attn_fwd_pipe3_kernel<128, ATTN_F16, true>(Params);
+template __global__ void attn_fwd_pipe3_kernel<128, ATTN_BF16, false>(Params);
+template __global__ void attn_fwd_pipe3_kernel<128, ATTN_BF16, true>(Params);
+
 }  // namespace kernels
 
 int launch_forward_d128(const Problem& p, hipStream_t stream) { return kernels::launch_16bit<128>(p, stream); }

@@ -35,6 +35,12 @@ template __global__ void attn_fwd_seq_kernel<64, ATTN_BF16, false, false, 128>(P
 template __global__ void attn_fwd_seq_kernel<64, ATTN_BF16, true, false, 32>(Params);
 template __global__ void attn_fwd_seq_kernel<64, ATTN_BF16, true, false, 128>(Params);
 
+// Three-stage pipelined variant.
+template __global__ void attn_fwd_pipe3_kernel<64, ATTN_F16, false>(Params);
+template __global__ void attn_fwd_pipe3_kernel<64, ATTN_F16, true>(Params);
+template __global__ void attn_fwd_pipe3_kernel<64, ATTN_BF16, false>(Params);
+template __global__ void attn_fwd_pipe3_kernel<64, ATTN_BF16, true>(Params);
+
 }  // namespace kernels
 
 int launch_forward_d64(const Problem& p, hipStream_t stream) { return kernels::launch_16bit<64>(p, stream); }

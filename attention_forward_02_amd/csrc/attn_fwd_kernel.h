@@ -955,6 +955,188 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_kernel(Pa
 }
 
 // ---------------------------------------------------------------------------
+// Three-stage pipelined kernel (16-bit, d = 64 and 128; a tuning variant):
+// the score MFMAs run two key tiles ahead of the P V MFMAs, so step j
+// overlaps the matrix work of S_{j+2} and of O += P_j V_j with the softmax
+// of tile j + 1 -- the three-stage form of the concept card's "Overlap of
+// matrix multiplies and softmax inside one warpgroup".  It holds one more
+// score tile and one more packed P than the two-stage kernel.
+//
+// References: P_{j+1} is formed against the reference m2 of its step, and a
+// raise decided from the row max of S_{j+2} reaches l at once (its next
+// term is P_{j+2}) but O only one step later, after P_{j+1} V_{j+1} has been
+// added against the old reference (the pending factor alpha_o).
+// K runs two tiles ahead of V: step j reads K_{j+2} and V_j from stage j % 2
+// of each ring while K_{j+3} and V_{j+1} stream into the other stage.
+// ---------------------------------------------------------------------------
+template <int D, int DT, bool CAUSAL, bool MASKED>
+__device__ __forceinline__ void step3(WaveState16<D, DT>& st, const LoopCtx& cx, int j, const i16x8 (&pj)[4],
+                                      i16x8 (&pn)[4], f32x16& s0, f32x16& s1, f32x16& n0, f32x16& n1, float& alpha_o,
+                                      bool& pend, const lds_t* Kn, const lds_t* Vs) {
+  // Phase A: S_{j+2} = K_{j+2} Q^T | P_{j+1} = exp2(c S_{j+1} - m2), packed
+  masked_scores<D, DT, CAUSAL, MASKED>(st, cx, j + 2, Kn, n0, n1);
+  const float mref = (st.m2 == -__builtin_inff()) ? 0.f : st.m2;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cx.c, -mref));
+    s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cx.c, -mref));
+  }
+  pn[0] = pack8<DT>(s0, 0);
+  pn[1] = pack8<DT>(s0, 8);
+  pn[2] = pack8<DT>(s1, 0);
+  pn[3] = pack8<DT>(s1, 8);
+  constexpr int kValuA = (80 + D / 8 - 1) / (D / 8);
+  ATTN_INTERLEAVE(3, D / 8, kValuA, 1);
+  // Phase B: O += P_j V_j | l += rowsum(P_{j+1}), row max of S_{j+2} and the
+  // reference update
+  pv_tile<D, DT>(st, pj, Vs);
+  if constexpr (DT == ATTN_F16) {
+    st.lrun += row_sum_f16<4>(pn);
+  } else {
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      ls0 += s0[r];
+      ls1 += s1[r];
+    }
+    st.lrun += ls0 + ls1;
+  }
+  bool rescale;
+  const float alpha = update_reference(st.m2, tile_max2(n0, n1, cx.c), rescale);
+  constexpr int kValuB = ((DT == ATTN_F16 ? 48 : 64) + D / 8 - 1) / (D / 8);
+  ATTN_INTERLEAVE(4, D / 8, kValuB, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  if (pend || rescale) {
+    asm volatile("" ::: "memory");  // keep the branch (see step)
+    st.lrun *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha_o;
+  }
+  alpha_o = alpha;
+  pend = rescale;
+}
+
+template <int D, int DT, bool CAUSAL>
+__global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_pipe3_kernel(Params p) {
+  static_assert(DT != ATTN_FP8_E4M3 && D != 256, "three-stage kernel: 16-bit, d = 64 or 128");
+  constexpr int kWaves = Waves<D, DT>::value;
+  constexpr int kBlockM = kWaves * kRowsPerWave;
+  constexpr int kRowBytes = D * 2;
+  constexpr int kTileBytes = kBlockN * kRowBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st1[kTileBytes];
+  lds_t* const K0 = (lds_t*)k_st0;
+  lds_t* const K1 = (lds_t*)k_st1;
+  lds_t* const V0 = (lds_t*)v_st0;
+  lds_t* const V1 = (lds_t*)v_st1;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int bh, qt;
+  schedule(p, blockIdx.x, CAUSAL, bh, qt);
+  const int q0 = qt * kBlockM;
+  LoopCtx cx;
+  cx.qw0 = q0 + wave * kRowsPerWave;
+  cx.qrow = cx.qw0 + (lane & 31);
+  cx.diag = p.Nk - p.Nq;
+  cx.Nk = p.Nk;
+  cx.half = lane >> 5;
+  cx.c = p.c;
+  cx.wave_kend = CAUSAL ? cx.qw0 + kRowsPerWave - 1 + cx.diag : p.Nk;
+  int kend = p.Nk;
+  if (CAUSAL) kend = min(p.Nk, q0 + kBlockM + cx.diag);
+  const int nt = kend > 0 ? (kend + kBlockN - 1) / kBlockN : 0;
+  cx.nt = nt;
+
+  const uint32_t head_bytes = (uint32_t)p.Nk * kRowBytes;
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(p.k + (size_t)bh * p.Nk * kRowBytes, head_bytes);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(p.v + (size_t)bh * p.Nk * kRowBytes, head_bytes);
+  TileLoader<D, DT, kWaves> ld;
+  ld.init(wave, lane);
+  WaveState16<D, DT> st;
+  st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane, p.q_and, p.q_xor);
+
+  if (nt > 0) {
+    const int tb = first_bias_tile<CAUSAL>(cx);
+    // Prologue: S_0 and its reference; S_1, P_0 and the reference after
+    // S_1.  K_1 is loaded even past the end (rows past Nk arrive as zeros),
+    // so every K stage a step reads holds finite data: scores of tiles past
+    // the end are -inf through the mask bias.
+    ld.load(K0, Kr, 0);
+    ld.load(V0, Vr, 0);
+    ld.load(K1, Kr, kBlockN);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    f32x16 a0, a1, b0, b1;
+    i16x8 pa[4], pb[4];
+    bool rescale;
+    if (tb > 0) masked_scores<D, DT, CAUSAL, false>(st, cx, 0, K0, a0, a1);
+    else masked_scores<D, DT, CAUSAL, true>(st, cx, 0, K0, a0, a1);
+    update_reference(st.m2, tile_max2(a0, a1, cx.c), rescale);
+    if (tb > 1) masked_scores<D, DT, CAUSAL, false>(st, cx, 1, K1, b0, b1);
+    else masked_scores<D, DT, CAUSAL, true>(st, cx, 1, K1, b0, b1);
+    {
+      const float mref = (st.m2 == -__builtin_inff()) ? 0.f : st.m2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        a0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(a0[r], cx.c, -mref));
+        a1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(a1[r], cx.c, -mref));
+      }
+      pa[0] = pack8<DT>(a0, 0);
+      pa[1] = pack8<DT>(a0, 8);
+      pa[2] = pack8<DT>(a1, 0);
+      pa[3] = pack8<DT>(a1, 8);
+      if constexpr (DT == ATTN_F16) {
+        st.lrun += row_sum_f16<4>(pa);
+      } else {
+        float ls = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ls += a0[r] + a1[r];
+        st.lrun += ls;
+      }
+    }
+    // l (the sum of P_0) moves to the new reference at once; O receives
+    // P_0 V_0, formed against the old one, in step 0 and moves after it
+    float alpha_o = update_reference(st.m2, tile_max2(b0, b1, cx.c), rescale);
+    st.lrun *= alpha_o;
+    bool pend = rescale;
+    __syncthreads();  // every wave is done with K_0's stage
+    if (2 < nt) ld.load(K0, Kr, 2 * kBlockN);
+    // Step j: P_j in (pa | pb), S_{j+1} in (b | a); steps j < jm score an
+    // unmasked tile j + 2.
+    auto two_steps = [&](int j, auto masked) -> bool {
+      constexpr bool M = decltype(masked)::value;
+      // even step: K_{j+2} in K0, V_j in V0; K_{j+3} -> K1, V_{j+1} -> V1
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (j + 3 < nt) ld.load(K1, Kr, (j + 3) * kBlockN);
+      if (j + 1 < nt) ld.load(V1, Vr, (j + 1) * kBlockN);
+      step3<D, DT, CAUSAL, M>(st, cx, j, pa, pb, b0, b1, a0, a1, alpha_o, pend, K0, V0);
+      if (j + 1 >= nt) return false;
+      // odd step: K_{j+3} in K1, V_{j+1} in V1; K_{j+4} -> K0, V_{j+2} -> V0
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (j + 4 < nt) ld.load(K0, Kr, (j + 4) * kBlockN);
+      if (j + 2 < nt) ld.load(V0, Vr, (j + 2) * kBlockN);
+      step3<D, DT, CAUSAL, M>(st, cx, j + 1, pb, pa, a0, a1, b0, b1, alpha_o, pend, K1, V1);
+      return true;
+    };
+    const int jm = tb > 2 ? (tb - 2) & ~1 : 0;
+    int j = 0;
+    for (; j < jm; j += 2) two_steps(j, BoolTag<false>{});
+    for (; j < nt; j += 2)
+      if (!two_steps(j, BoolTag<true>{})) break;
+    if (pend) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha_o;
+    }
+  }
+  store_output<D, DT>(p, st, bh, cx.qrow, cx.half);
+}
+
+// ---------------------------------------------------------------------------
 // Pingpong kernel (16-bit, d = 128): the pages' two-consumer schedule
 // (concept card, "Pingpong scheduling between two consumer warpgroups";
 // "Inside FlashAttention-3", section 3).  The workgroup's 8 waves form two
@@ -1812,6 +1994,7 @@ struct Variants {
   // d = 256 the four score accumulators do not fit beside O and Q)
   static constexpr bool bc32 = DT != ATTN_FP8_E4M3 && D != 256;
   static constexpr bool bc128 = D != 256;
+  static constexpr bool pipe3 = DT != ATTN_FP8_E4M3 && D != 256;
 };
 
 // The wide-wave kernels (attn_fwd_wide.h) live in a translation unit of
@@ -1915,6 +2098,12 @@ int launch_one(const Problem& pr, hipStream_t stream) {
       return ATTN_ERR_VARIANT;
     case ATTN_VARIANT_WIDE:
       if constexpr (Variants<D, DT>::wide) return launch_wide_d128(p, DT, CAUSAL, stream);
+      return ATTN_ERR_VARIANT;
+    case ATTN_VARIANT_PIPELINED_3STAGE:
+      if constexpr (Variants<D, DT>::pipe3) {
+        hipLaunchKernelGGL((attn_fwd_pipe3_kernel<D, DT, CAUSAL>), dim3(p.total_tiles), block, 0, stream, p);
+        break;
+      }
       return ATTN_ERR_VARIANT;
     case ATTN_VARIANT_SEQUENTIAL_BC32:
       if constexpr (Variants<D, DT>::bc32) {

@@ -38,7 +38,7 @@ ROOT = os.path.dirname(PKG)
 VARIANTS = [b.ATTN_VARIANT_AUTO, b.ATTN_VARIANT_PIPELINED, b.ATTN_VARIANT_PIPELINED_4STAGE,
             b.ATTN_VARIANT_SEQUENTIAL, b.ATTN_VARIANT_SPLIT, b.ATTN_VARIANT_PINGPONG,
             b.ATTN_VARIANT_PRODUCER, b.ATTN_VARIANT_WIDE, b.ATTN_VARIANT_SEQUENTIAL_BC32,
-            b.ATTN_VARIANT_SEQUENTIAL_BC128]
+            b.ATTN_VARIANT_SEQUENTIAL_BC128, b.ATTN_VARIANT_PIPELINED_3STAGE]
 
 
 def _agree(o, lse, o_ref, lse_ref, fp8):

@@ -114,7 +114,10 @@ enum {
  *   SEQUENTIAL_BC32    SEQUENTIAL with 32-key tiles (16-bit d = 64, 128)
  *   SEQUENTIAL_BC128   SEQUENTIAL with 128-key tiles: one row max,
  *                      reference update and barrier per 128 keys (d = 64,
- *                      128) */
+ *                      128)
+ *   PIPELINED_3STAGE   scores two key tiles ahead of P V, so each step
+ *                      overlaps both matrix products with the softmax of
+ *                      the tile between them (16-bit d = 64, 128) */
 enum {
   ATTN_VARIANT_AUTO = 0,
   ATTN_VARIANT_PIPELINED = 1,
@@ -125,7 +128,8 @@ enum {
   ATTN_VARIANT_PRODUCER = 6,
   ATTN_VARIANT_WIDE = 7,
   ATTN_VARIANT_SEQUENTIAL_BC32 = 8,
-  ATTN_VARIANT_SEQUENTIAL_BC128 = 9
+  ATTN_VARIANT_SEQUENTIAL_BC128 = 9,
+  ATTN_VARIANT_PIPELINED_3STAGE = 10
 };
 
 /*

@@ -151,7 +151,7 @@ def test_variant_codes_match_header():
     assert codes == {"ATTN_VARIANT_AUTO": 0, "ATTN_VARIANT_PIPELINED": 1, "ATTN_VARIANT_PIPELINED_4STAGE": 2,
                      "ATTN_VARIANT_SEQUENTIAL": 3, "ATTN_VARIANT_SPLIT": 4, "ATTN_VARIANT_PINGPONG": 5,
                      "ATTN_VARIANT_PRODUCER": 6, "ATTN_VARIANT_WIDE": 7, "ATTN_VARIANT_SEQUENTIAL_BC32": 8,
-                     "ATTN_VARIANT_SEQUENTIAL_BC128": 9}
+                     "ATTN_VARIANT_SEQUENTIAL_BC128": 9, "ATTN_VARIANT_PIPELINED_3STAGE": 10}
     for name, val in codes.items():
         assert getattr(b, name) == val
 
@@ -176,6 +176,8 @@ def test_variant_availability_table():
                 want.add(b.ATTN_VARIANT_SEQUENTIAL_BC32)
             if d != 256:
                 want.add(b.ATTN_VARIANT_SEQUENTIAL_BC128)
+            if d != 256 and dt != b.ATTN_FP8_E4M3:
+                want.add(b.ATTN_VARIANT_PIPELINED_3STAGE)
             assert got == want, (d, dt, got)
     assert not lib.attn_variant_available(96, b.ATTN_F16, 0) and not lib.attn_variant_available(64, 5, 0)
 
@@ -189,6 +191,7 @@ def test_variant_availability_table():
     (dict(d=128, dtype=2, variant=7), b.ATTN_ERR_VARIANT), (dict(d=128, variant=15), b.ATTN_ERR_VARIANT),
     (dict(dtype=2, variant=8), b.ATTN_ERR_VARIANT), (dict(d=256, variant=8), b.ATTN_ERR_VARIANT),
     (dict(d=256, variant=9), b.ATTN_ERR_VARIANT), (dict(d=256, dtype=2, variant=9), b.ATTN_ERR_VARIANT),
+    (dict(dtype=2, variant=10), b.ATTN_ERR_VARIANT), (dict(d=256, variant=10), b.ATTN_ERR_VARIANT),
     (dict(q=None, variant=1), b.ATTN_ERR_NULL), (dict(d=80, variant=1), b.ATTN_ERR_HEADDIM),
     (dict(dtype=2, kd=0.0), b.ATTN_ERR_SCALE), (dict(lse=O + 64), b.ATTN_ERR_ALIAS),
 ])

@@ -51,7 +51,7 @@ def test_tuner_times_every_variant():
     rows = tuner.tune(q, k, v, True, float(inp.scale), reps=3, rounds=2, settle_s=0.05)
     names = [r["name"] for r in rows]
     assert names[0] == "auto" and set(names) == {"auto", "pipelined", "pipelined_4stage", "sequential", "split",
-                                                 "sequential_bc32", "sequential_bc128"}
+                                                 "sequential_bc32", "sequential_bc128", "pipelined_3stage"}
     for r in rows:
         assert r["ms"] is not None and r["ms"] > 0, r
     timed = [r["ms"] for r in rows[1:]]

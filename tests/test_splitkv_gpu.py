@@ -1,7 +1,7 @@
 """GPU parity of the split-key forward (attn_fwd_splitkv) against the oracle.
 
 The key range of each query tile is split over several workgroups whose
-partial results (O, m, l) are merged by the last one to finish with the
+partial results (O, m, l) a second kernel merges in split order with the
 online-softmax rescale.  Covered, through the C ABI:
 * every head dim, input format and causality, with the library's split
   choice and with forced split counts (two, three, and more splits than the

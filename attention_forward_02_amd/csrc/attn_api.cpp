@@ -55,7 +55,7 @@ bool variant_available(int d, int dtype, int variant) {
     case ATTN_VARIANT_SPLIT:
       return d == 64 && dtype != ATTN_FP8_E4M3;
     case ATTN_VARIANT_PINGPONG:
-      return d == 128 && dtype != ATTN_FP8_E4M3;
+      return d == 128;
     case ATTN_VARIANT_PRODUCER:
       return d == 128;
     case ATTN_VARIANT_WIDE:

@@ -19,6 +19,8 @@ template __global__ void attn_fwd_kernel<128, ATTN_FP8_E4M3, false, 4>(Params);
 template __global__ void attn_fwd_kernel<128, ATTN_FP8_E4M3, true, 4>(Params);
 template __global__ void attn_fwd_producer_kernel<128, ATTN_FP8_E4M3, false, 2, 1>(Params);
 template __global__ void attn_fwd_producer_kernel<128, ATTN_FP8_E4M3, true, 2, 1>(Params);
+template __global__ void attn_fwd_pingpong_kernel<128, ATTN_FP8_E4M3, false>(Params);
+template __global__ void attn_fwd_pingpong_kernel<128, ATTN_FP8_E4M3, true>(Params);
 
 // Key-tile-size variant of the sequential kernel.
 template __global__ void attn_fwd_seq_kernel<128, ATTN_FP8_E4M3, false, false, 128>(Params);

@@ -29,7 +29,7 @@
 //   * exp is v_exp_f32 (2^x) on scores pre-multiplied by scale * log2(e);
 //     LSE is converted back to natural log at the end.
 //
-// Four kernels share these pieces:
+// The four default kernels share these pieces:
 //   * attn_fwd_producer_kernel (binary16 d = 128): eight consumer waves run
 //     the sequential step below while a ninth, producer wave streams K and
 //     V into the LDS ring;
@@ -39,17 +39,21 @@
 //     row max (the pages' two-stage overlap of matrix multiplies and
 //     softmax), while the SIMD's second wave fills the matrix core from its
 //     own step;
-//   * attn_fwd_seq_kernel (E4M3 d = 128, every d = 256, and the
-//     block-scaled E4M3 variant): the same loop without the pipelined score
-//     tile, for a step bound by softmax VALU work or by registers;
+//   * attn_fwd_seq_kernel (E4M3 d = 128 with 128-key tiles, every d = 256,
+//     and the block-scaled E4M3 variant): the same loop without the
+//     pipelined score tile, for a step bound by softmax VALU work or by
+//     registers;
 //   * attn_fwd_split_kernel (16-bit d = 64, mid-size grids): two wave groups
 //     walk the two halves of the key range and merge.
 // Those are the defaults (launch_one).  Every kernel built for a (d,
 // format) can also be requested explicitly as a tuning variant, including
-// the pipelined kernel with a four-stage K/V ring and, at 16-bit d = 128,
-// attn_fwd_pingpong_kernel (the pages' explicit two-group pingpong) and
-// attn_fwd_wide_kernel (64 query rows per wave, one wave per SIMD;
-// attn_fwd_wide.h, its own translation unit).
+// the pipelined kernel with a four-stage K/V ring, the three-stage
+// pipelined kernel (attn_fwd_pipe3_kernel), the sequential kernel with 32-
+// or 128-key tiles, at d = 128 attn_fwd_pingpong_kernel (the pages'
+// explicit two-group pingpong) and, at 16-bit d = 128, attn_fwd_wide_kernel
+// (64 query rows per wave, one wave per SIMD; attn_fwd_wide.h, its own
+// translation unit).  The split-key forward across workgroups is in
+// attn_fwd_splitkv.h.
 // Masking is folded into the initial values of the score accumulators; the
 // key loops run the unmasked steps and the masked ones (ragged end, causal
 // diagonal) as two loops of one step variant each, so every step is one
@@ -1137,7 +1141,7 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_pipe3_ker
 }
 
 // ---------------------------------------------------------------------------
-// Pingpong kernel (16-bit, d = 128): the pages' two-consumer schedule
+// Pingpong kernel (d = 128, every format): the pages' two-consumer schedule
 // (concept card, "Pingpong scheduling between two consumer warpgroups";
 // "Inside FlashAttention-3", section 3).  The workgroup's 8 waves form two
 // groups, A = waves 0-3 and B = waves 4-7, so every SIMD holds one wave of
@@ -1157,24 +1161,54 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_pipe3_ker
 // groups finished reading one half earlier; A waits for its share at the end
 // of its next softmax half, B at the end of its MFMA half j.
 // ---------------------------------------------------------------------------
+// P of one tile as the P V MFMA's B operand: four 16-key fragments at 16
+// bits, one 64-key fragment for E4M3.
+template <int DT>
+struct PTile {
+  i16x8 f[4];
+};
+template <>
+struct PTile<ATTN_FP8_E4M3> {
+  i32x8 f;
+};
+
 template <int D, int DT, bool CAUSAL, bool MASKED, bool PV>
-__device__ __forceinline__ void pp_mfma_half(WaveState16<D, DT>& st, const LoopCtx& cx, int j, const i16x8 (&pf)[4],
+__device__ __forceinline__ void pp_mfma_half(WaveState<D, DT>& st, const LoopCtx& cx, int j, const PTile<DT>& pt,
                                              f32x16& s0, f32x16& s1, const lds_t* Kn, const lds_t* Vc) {
   __builtin_amdgcn_s_setprio(1);
   masked_scores<D, DT, CAUSAL, MASKED>(st, cx, j + 1, Kn, s0, s1);
-  if constexpr (PV) pv_tile<D, DT>(st, pf, Vc);
-  // scores: 3 K reads ahead, one per MFMA; P V: 4 V reads ahead, two per MFMA
-  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+  if constexpr (DT == ATTN_FP8_E4M3) {
+    if constexpr (PV) pv_tile<D>(st, pt.f, Vc);
+    // scores: two 16-byte K reads per 64-cycle MFMA, one MFMA's worth
+    // ahead; P V: the four transpose reads of the next MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-  for (int i = 0; i < 2 * D / 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  if constexpr (PV) {
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
+    for (int i = 0; i < 2 * D / 64; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    if constexpr (PV) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+    }
+  } else {
+    if constexpr (PV) pv_tile<D, DT>(st, pt.f, Vc);
+    // scores: 3 K reads ahead, one per MFMA; P V: 4 V reads ahead, two per MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * D / 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (PV) {
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -1182,8 +1216,8 @@ __device__ __forceinline__ void pp_mfma_half(WaveState16<D, DT>& st, const LoopC
 }
 
 template <int D, int DT>
-__device__ __forceinline__ void pp_softmax_half(WaveState16<D, DT>& st, const LoopCtx& cx, f32x16& s0, f32x16& s1,
-                                                i16x8 (&pf)[4]) {
+__device__ __forceinline__ void pp_softmax_half(WaveState<D, DT>& st, const LoopCtx& cx, f32x16& s0, f32x16& s1,
+                                                PTile<DT>& pt) {
   bool rescale;
   const float alpha = update_reference(st.m2, tile_max2(s0, s1, cx.c), rescale);
   if (rescale) {
@@ -1198,13 +1232,18 @@ __device__ __forceinline__ void pp_softmax_half(WaveState16<D, DT>& st, const Lo
     s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cx.c, -mref));
     s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cx.c, -mref));
   }
-  pf[0] = pack8<DT>(s0, 0);
-  pf[1] = pack8<DT>(s0, 8);
-  pf[2] = pack8<DT>(s1, 0);
-  pf[3] = pack8<DT>(s1, 8);
-  if constexpr (DT == ATTN_F16) {
-    st.lrun += row_sum_f16<4>(pf);
+  if constexpr (DT == ATTN_FP8_E4M3) {
+    pt.f = pack_p_fp8(s0, s1);
   } else {
+    pt.f[0] = pack8<DT>(s0, 0);
+    pt.f[1] = pack8<DT>(s0, 8);
+    pt.f[2] = pack8<DT>(s1, 0);
+    pt.f[3] = pack8<DT>(s1, 8);
+  }
+  if constexpr (DT == ATTN_F16) {
+    st.lrun += row_sum_f16<4>(pt.f);
+  } else {
+    // bfloat16 and E4M3: the unrounded p
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -1217,10 +1256,10 @@ __device__ __forceinline__ void pp_softmax_half(WaveState16<D, DT>& st, const Lo
 
 template <int D, int DT, bool CAUSAL>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) attn_fwd_pingpong_kernel(Params p) {
-  static_assert(D == 128 && DT != ATTN_FP8_E4M3, "pingpong kernel: 16-bit, d = 128");
+  static_assert(D == 128, "pingpong kernel: d = 128");
   constexpr int kWaves = 8;
   constexpr int kBlockM = kWaves * kRowsPerWave;
-  constexpr int kRowBytes = D * 2;
+  constexpr int kRowBytes = D * Fmt<DT>::kBytes;
   constexpr int kTileBytes = kBlockN * kRowBytes;
   __shared__ __attribute__((aligned(1024))) unsigned char k_st0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char k_st1[kTileBytes];
@@ -1256,7 +1295,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) a
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(p.v + (size_t)bh * p.Nk * kRowBytes, head_bytes);
   TileLoader<D, DT, kWaves> ld;
   ld.init(wave, lane);
-  WaveState16<D, DT> st;
+  WaveState<D, DT> st;
   st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane, p.q_and, p.q_xor);
 
   if (nt > 0) {
@@ -1268,7 +1307,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) a
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     f32x16 s0, s1;
-    i16x8 pf[4];
+    PTile<DT> pf;
     const int tb = first_bias_tile<CAUSAL>(cx);
     if (grp == 1) __syncthreads();
     // MFMA half -1: S_0 only
@@ -1986,7 +2025,7 @@ template <int D, int DT>
 struct Variants {
   static constexpr bool pipelined = D != 256;
   static constexpr bool split = UseSplit<D, DT>::value;
-  static constexpr bool pingpong = D == 128 && DT != ATTN_FP8_E4M3;
+  static constexpr bool pingpong = D == 128;
   static constexpr bool producer = D == 128;
   static constexpr bool wide = D == 128 && DT != ATTN_FP8_E4M3;
   // key-tile-size axis of the sequential kernel: 32 keys (16-bit d = 64,

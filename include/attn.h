@@ -103,7 +103,7 @@ enum {
  *   PINGPONG           two wave groups alternating matrix-only and
  *                      softmax-only halves of each step behind workgroup
  *                      barriers, so that one group's softmax runs under the
- *                      other's MFMAs (16-bit d = 128)
+ *                      other's MFMAs (d = 128)
  *   PRODUCER           a ninth, producer wave streams K and V into a
  *                      2-stage ring; the eight consumer waves run the
  *                      sequential step on tiles already in LDS (d = 128)

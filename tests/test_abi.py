@@ -166,7 +166,7 @@ def test_variant_availability_table():
                 want |= {b.ATTN_VARIANT_PIPELINED, b.ATTN_VARIANT_PIPELINED_4STAGE}
             if d == 64 and dt != b.ATTN_FP8_E4M3:
                 want.add(b.ATTN_VARIANT_SPLIT)
-            if d == 128 and dt != b.ATTN_FP8_E4M3:
+            if d == 128:
                 want.add(b.ATTN_VARIANT_PINGPONG)
             if d == 128:
                 want.add(b.ATTN_VARIANT_PRODUCER)
@@ -186,7 +186,7 @@ def test_variant_availability_table():
     (dict(variant=5), b.ATTN_ERR_VARIANT), (dict(variant=-1), b.ATTN_ERR_VARIANT),
     (dict(d=256, variant=1), b.ATTN_ERR_VARIANT), (dict(d=256, variant=2), b.ATTN_ERR_VARIANT),
     (dict(dtype=2, variant=4), b.ATTN_ERR_VARIANT), (dict(d=128, variant=4), b.ATTN_ERR_VARIANT),
-    (dict(variant=5), b.ATTN_ERR_VARIANT), (dict(d=128, dtype=2, variant=5), b.ATTN_ERR_VARIANT),
+    (dict(variant=5), b.ATTN_ERR_VARIANT), (dict(d=256, dtype=2, variant=5), b.ATTN_ERR_VARIANT),
     (dict(variant=6), b.ATTN_ERR_VARIANT), (dict(variant=7), b.ATTN_ERR_VARIANT),
     (dict(d=128, dtype=2, variant=7), b.ATTN_ERR_VARIANT), (dict(d=128, variant=15), b.ATTN_ERR_VARIANT),
     (dict(dtype=2, variant=8), b.ATTN_ERR_VARIANT), (dict(d=256, variant=8), b.ATTN_ERR_VARIANT),

@@ -19,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
+# Standalone probe of the chip's MFMA and VALU ceilings (not part of the library).
+CEILING = os.path.join(PKG, "chip_ceiling")
 ARCH = "gfx950"
 
 COMMON = [
@@ -96,6 +98,9 @@ def build(verbose=False):
         out = LIB + ".tmp"
         _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out], verbose)
         os.replace(out, LIB)
+        exe = os.path.join(tmp, "chip_ceiling")
+        _run([hipcc(), *[f for f in COMMON if f != "-fPIC"], os.path.join(CSRC, "chip_ceiling.hip"), "-o", exe], verbose)
+        shutil.move(exe, CEILING)
     return LIB
 
 

@@ -69,6 +69,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn.h"
 #include "attn_internal.h"
 
@@ -285,6 +287,13 @@ struct TileLoader {
                                                voff[i] + tile, 0, 0, 0);
   }
 };
+
+// Wait until at most N vector-memory loads of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit counter");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Buffer resource over `bytes` bytes at `base` (raw, stride 0; gfx9 word 3).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -1156,10 +1165,11 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_pipe3_ker
 // half overwrites it, so a wave holds one score tile (fewer registers than
 // the pipelined kernel's two).
 //
-// Ring: K and V in two stages each.  K_{j+2} and V_{j+1} are loaded at the
-// start of A's MFMA half j (= B's softmax half j) into the stages both
-// groups finished reading one half earlier; A waits for its share at the end
-// of its next softmax half, B at the end of its MFMA half j.
+// Ring: K and V in NS stages each (two built; three measured no faster).
+// K_{j+NS} and V_{j+NS-1} are loaded at the start of A's MFMA half j (= B's
+// softmax half j) into the stages both groups finished reading one half
+// earlier; A waits for its share at the end of its softmax half before the
+// MFMA half that reads them, B at the end of its MFMA half before that.
 // ---------------------------------------------------------------------------
 // P of one tile as the P V MFMA's B operand: four 16-key fragments at 16
 // bits, one 64-key fragment for E4M3.
@@ -1254,21 +1264,16 @@ __device__ __forceinline__ void pp_softmax_half(WaveState<D, DT>& st, const Loop
   }
 }
 
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool CAUSAL, int NS = 2>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) attn_fwd_pingpong_kernel(Params p) {
   static_assert(D == 128, "pingpong kernel: d = 128");
+  static_assert(NS == 2 || NS == 3, "two or three ring stages");
   constexpr int kWaves = 8;
   constexpr int kBlockM = kWaves * kRowsPerWave;
   constexpr int kRowBytes = D * Fmt<DT>::kBytes;
   constexpr int kTileBytes = kBlockN * kRowBytes;
-  __shared__ __attribute__((aligned(1024))) unsigned char k_st0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char k_st1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_st0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_st1[kTileBytes];
-  lds_t* const K0 = (lds_t*)k_st0;
-  lds_t* const K1 = (lds_t*)k_st1;
-  lds_t* const V0 = (lds_t*)v_st0;
-  lds_t* const V1 = (lds_t*)v_st1;
+  __shared__ __attribute__((aligned(1024))) unsigned char k_st[NS][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_st[NS][kTileBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1293,17 +1298,20 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) a
   const uint32_t head_bytes = (uint32_t)p.Nk * kRowBytes;
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc(p.k + (size_t)bh * p.Nk * kRowBytes, head_bytes);
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(p.v + (size_t)bh * p.Nk * kRowBytes, head_bytes);
-  TileLoader<D, DT, kWaves> ld;
+  using Loader = TileLoader<D, DT, kWaves>;
+  constexpr int kLoads = 2 * Loader::kPerWave;  // a wave's loads per batch (its share of one K and one V tile)
+  Loader ld;
   ld.init(wave, lane);
   WaveState<D, DT> st;
   st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane, p.q_and, p.q_xor);
 
   if (nt > 0) {
-    // K_1 is loaded even when there is no tile 1 (zeros past the end), so
-    // every K stage an MFMA half reads holds finite data.
-    ld.load(K0, Kr, 0);
-    ld.load(V0, Vr, 0);
-    ld.load(K1, Kr, kBlockN);
+    // K_0 .. K_{NS-1} and V_0 .. V_{NS-2}, also past the last tile (zeros),
+    // so that every K stage an MFMA half reads holds finite data.
+#pragma unroll
+    for (int s = 0; s < NS; ++s) ld.load((lds_t*)k_st[s], Kr, s * kBlockN);
+#pragma unroll
+    for (int s = 0; s + 1 < NS; ++s) ld.load((lds_t*)v_st[s], Vr, s * kBlockN);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     f32x16 s0, s1;
@@ -1311,54 +1319,62 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) a
     const int tb = first_bias_tile<CAUSAL>(cx);
     if (grp == 1) __syncthreads();
     // MFMA half -1: S_0 only
-    if (tb > 0) pp_mfma_half<D, DT, CAUSAL, false, false>(st, cx, -1, pf, s0, s1, K0, V0);
-    else pp_mfma_half<D, DT, CAUSAL, true, false>(st, cx, -1, pf, s0, s1, K0, V0);
+    if (tb > 0) pp_mfma_half<D, DT, CAUSAL, false, false>(st, cx, -1, pf, s0, s1, (const lds_t*)k_st[0], nullptr);
+    else pp_mfma_half<D, DT, CAUSAL, true, false>(st, cx, -1, pf, s0, s1, (const lds_t*)k_st[0], nullptr);
     __syncthreads();
-    // Halves softmax(j), MFMA(j), softmax(j+1), MFMA(j+1) for even j;
-    // returns false after the last MFMA half.
-    auto four_halves = [&](int j, auto masked) -> bool {
-      constexpr bool M = decltype(masked)::value;
-      // softmax(j); B loads K_{j+2} -> K0, V_{j+1} -> V1
-      if (grp == 1) {
-        if (j + 2 < nt) ld.load(K0, Kr, (j + 2) * kBlockN);
-        if (j + 1 < nt) ld.load(V1, Vr, (j + 1) * kBlockN);
-      }
-      pp_softmax_half<D, DT>(st, cx, s0, s1, pf);
-      if (grp == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      // MFMA(j): P_j V_j (V0), S_{j+1} (K1); A loads as B did above
-      if (grp == 0) {
-        if (j + 2 < nt) ld.load(K0, Kr, (j + 2) * kBlockN);
-        if (j + 1 < nt) ld.load(V1, Vr, (j + 1) * kBlockN);
-      }
-      pp_mfma_half<D, DT, CAUSAL, M, true>(st, cx, j, pf, s0, s1, K1, V0);
-      if (grp == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (j + 1 >= nt) return false;
-      // softmax(j+1); B loads K_{j+3} -> K1, V_{j+2} -> V0
-      if (grp == 1) {
-        if (j + 3 < nt) ld.load(K1, Kr, (j + 3) * kBlockN);
-        if (j + 2 < nt) ld.load(V0, Vr, (j + 2) * kBlockN);
-      }
-      pp_softmax_half<D, DT>(st, cx, s0, s1, pf);
-      if (grp == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      // MFMA(j+1): P_{j+1} V_{j+1} (V1), S_{j+2} (K0)
-      if (grp == 0) {
-        if (j + 3 < nt) ld.load(K1, Kr, (j + 3) * kBlockN);
-        if (j + 2 < nt) ld.load(V0, Vr, (j + 2) * kBlockN);
-      }
-      pp_mfma_half<D, DT, CAUSAL, M, true>(st, cx, j + 1, pf, s0, s1, K0, V1);
-      if (grp == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      return j + 2 < nt;
+    // Batch t (issued by group A at the start of its MFMA half t and by
+    // group B at the start of its softmax half t, the same half of the
+    // schedule): K_{t+NS} into the stage K_t left (scored in MFMA half
+    // t - 1) and V_{t+NS-1} into the stage V_{t-1} left.  The data of MFMA
+    // half t (K_{t+1}, V_t) come from batch t + 1 - NS; when it must have
+    // landed, each wave has issued NS - 2 batches since, all full unless
+    // the tiles ran out (then it waits for everything).
+    auto issue = [&](int t, lds_t* Kd, lds_t* Vd) {
+      if (t + NS < nt) ld.load(Kd, Kr, (t + NS) * kBlockN);
+      if (t + NS - 1 < nt) ld.load(Vd, Vr, (t + NS - 1) * kBlockN);
     };
-    // The MFMA halves of a pair score tiles j+1 and j+2: unmasked while both
-    // lie before the first tile that needs a mask bias.
-    int j = 0;
-    for (; j + 2 < tb; j += 2) four_halves(j, BoolTag<false>{});
-    for (; j < nt; j += 2)
-      if (!four_halves(j, BoolTag<true>{})) break;
+    auto wait_batches = [&](bool full) {
+      if constexpr (NS == 3) {
+        if (full) {
+          wait_vmcnt<kLoads>();
+          return;
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    // Softmax half t, then MFMA half t: P_t V_t (V stage t % NS) and
+    // S_{t+1} (K stage (t + 1) % NS); R = t % NS.  Returns false after the
+    // last MFMA half.
+    auto pair = [&](int t, auto r, auto masked) -> bool {
+      constexpr int R = decltype(r)::value;
+      constexpr bool M = decltype(masked)::value;
+      lds_t* const Kd = (lds_t*)k_st[R];
+      lds_t* const Vd = (lds_t*)v_st[(R + NS - 1) % NS];
+      if (grp == 1) issue(t, Kd, Vd);
+      pp_softmax_half<D, DT>(st, cx, s0, s1, pf);
+      if (grp == 0) wait_batches(t + NS - 1 < nt);
+      __syncthreads();
+      if (grp == 0) issue(t, Kd, Vd);
+      pp_mfma_half<D, DT, CAUSAL, M, true>(st, cx, t, pf, s0, s1, (const lds_t*)k_st[(R + 1) % NS],
+                                           (const lds_t*)v_st[R]);
+      if (grp == 1) wait_batches(t + NS < nt);
+      __syncthreads();
+      return t + 1 < nt;
+    };
+    // The MFMA halves of tiles t .. t + NS - 1 score tiles t + 1 .. t + NS:
+    // unmasked while all lie before the first tile that needs a mask bias.
+    auto round = [&](int t, auto masked) -> bool {
+      if (!pair(t, std::integral_constant<int, 0>{}, masked)) return false;
+      if (!pair(t + 1, std::integral_constant<int, 1>{}, masked)) return false;
+      if constexpr (NS == 3) {
+        if (!pair(t + 2, std::integral_constant<int, 2>{}, masked)) return false;
+      }
+      return true;
+    };
+    int t = 0;
+    for (; t + NS < tb; t += NS) round(t, BoolTag<false>{});
+    for (; t < nt; t += NS)
+      if (!round(t, BoolTag<true>{})) break;
     if (grp == 0) __syncthreads();
   }
   store_output<D, DT>(p, st, bh, cx.qrow, cx.half);
@@ -1758,11 +1774,6 @@ attn_fwd_seq_kernel(Params p) {
 // j + NS - 1.  The consumers need at most 168 VGPRs, so three waves share a
 // SIMD and the extra waves fit beside the eight.
 // ---------------------------------------------------------------------------
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit counter");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 template <int D, int DT, bool CAUSAL, int NS, int NP>
 __global__ void __launch_bounds__(64 * (8 + NP)) attn_fwd_producer_kernel(Params p) {

@@ -20,6 +20,11 @@
 //   exp        waves 0-3 only: 16 v_exp_f32 (+ 16 multiplies) per iteration
 //   mfma f16 + fma / + exp: waves 0-3 the f16 MFMA loop, waves 4-7 (same
 //              SIMDs) the fma or exp loop at the same time
+//   mfma f16 + lds (+ fma / + exp): the MFMA waves take their A operands
+//              from LDS, one 16-byte read per MFMA (1 KB per wave
+//              instruction, 32 bytes per MFMA cycle: the operand rate of
+//              the attention kernels' score and P V products), read one
+//              iteration ahead
 //
 // The MFMA operands are distinct per lane and the accumulators feed back,
 // so no iteration can be folded away.
@@ -36,18 +41,59 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-enum { kMfmaF16 = 0, kMfmaFp8 = 1, kFma = 2, kExp = 3, kMfmaFma = 4, kMfmaExp = 5, kTests = 6 };
+enum { kMfmaF16 = 0, kMfmaFp8 = 1, kFma = 2, kExp = 3, kMfmaFma = 4, kMfmaExp = 5, kLds = 6, kLdsFma = 7, kLdsExp = 8 };
 constexpr int kCUs = 256;
 constexpr int kWaves = 8;
 
 template <int T>
 __global__ void __launch_bounds__(512) ceiling_kernel(float* sink, long long* cycles, int iters) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const bool mfma_wave = (T == kMfmaF16 || T == kMfmaFp8) || ((T == kMfmaFma || T == kMfmaExp) && w < 4);
-  const bool valu_wave = ((T == kFma || T == kExp) && w < 4) || ((T == kMfmaFma || T == kMfmaExp) && w >= 4);
+  constexpr bool kPair = T == kMfmaFma || T == kMfmaExp || T == kLdsFma || T == kLdsExp;
+  constexpr bool kUsesLds = T == kLds || T == kLdsFma || T == kLdsExp;
+  constexpr bool kExpLoop = T == kExp || T == kMfmaExp || T == kLdsExp;
+  const bool mfma_wave = (T == kMfmaF16 || T == kMfmaFp8 || T == kLds) || (kPair && w < 4);
+  const bool valu_wave = ((T == kFma || T == kExp) && w < 4) || (kPair && w >= 4);
+  constexpr int kLdsBytes = 16384;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kUsesLds ? kLdsBytes : 16];
+  if constexpr (kUsesLds) {
+    for (int i = threadIdx.x; i < kLdsBytes / 2; i += 512)
+      ((_Float16*)lds)[i] = (_Float16)(0.001f * (i & 255));
+    __syncthreads();
+  }
   float acc = 0.f;
   const long long t0 = __builtin_readcyclecounter();
-  if (mfma_wave) {
+  if (mfma_wave && kUsesLds) {
+    f16x8 b;
+    for (int i = 0; i < 8; ++i) b[i] = (_Float16)(0.25f - 0.002f * (lane - 3 * i));
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    typedef _Float16 lds_f16x8 __attribute__((ext_vector_type(8), address_space(3)));
+    const lds_f16x8* base = (const lds_f16x8*)(lds + 16 * lane);
+    // operand of MFMA i of iteration it: 1 KB block (4 it + i) mod 16; two
+    // register sets, each read one iteration before its MFMAs
+    f16x8 a[4], n[4];
+    for (int i = 0; i < 4; ++i) a[i] = base[64 * i];
+    auto read = [&](f16x8(&r)[4], int it) {
+      const int nb = (it & 3) * 4 * 64;
+      for (int i = 0; i < 4; ++i) r[i] = base[nb + 64 * i];
+    };
+    auto mfma4 = [&](const f16x8(&r)[4]) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(r[0], b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(r[1], b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(r[2], b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(r[3], b, c3, 0, 0, 0);
+    };
+    for (int it = 0; it < iters; it += 2) {
+      read(n, it + 1);
+      mfma4(a);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      read(a, it + 2);
+      mfma4(n);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    for (int i = 0; i < 16; ++i) acc += c0[i] + c1[i] + c2[i] + c3[i];
+  } else if (mfma_wave) {
     f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
     if constexpr (T == kMfmaFp8) {
       i32x8 a, b;
@@ -80,11 +126,11 @@ __global__ void __launch_bounds__(512) ceiling_kernel(float* sink, long long* cy
     for (int i = 0; i < 16; ++i) x[i] = 0.01f * lane + i;
     // the VALU waves run twice the MFMA waves' iterations in the overlap
     // tests, so that they are busy for the whole MFMA loop
-    const int n = (T == kMfmaFma || T == kMfmaExp) ? 2 * iters : iters;
+    const int n = kPair ? 2 * iters : iters;
     for (int it = 0; it < n; ++it) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if constexpr (T == kFma || T == kMfmaFma) {
+        if constexpr (!kExpLoop) {
           x[i] = __builtin_fmaf(x[i], 0.999f, 0.001f);
           x[i] = __builtin_fmaf(x[i], 0.999f, 0.001f);
         } else {
@@ -140,7 +186,7 @@ Result run(int iters, double seconds, float* sink, long long* cyc) {
   CHECK(hipGetLastError());
   std::vector<long long> c(kCUs * kWaves);
   CHECK(hipMemcpy(c.data(), cyc, c.size() * sizeof(long long), hipMemcpyDeviceToHost));
-  const bool both = T == kMfmaFma || T == kMfmaExp;
+  const bool both = T == kMfmaFma || T == kMfmaExp || T == kLdsFma || T == kLdsExp;
   const bool valu_only = T == kFma || T == kExp;
   double mc = 0, vc = 0, maxc = 0;
   for (int b = 0; b < kCUs; ++b)
@@ -203,6 +249,9 @@ int main(int argc, char** argv) {
   row("exp (16 exp + 16 mul per iteration)", run<kExp>(iters, seconds, sink, cyc), 0, 0, 0, false);
   row("mfma f16 + fma on the same SIMDs", run<kMfmaFma>(iters, seconds, sink, cyc), f16_flop, 2516.6, 4, false);
   row("mfma f16 + exp on the same SIMDs", run<kMfmaExp>(iters, seconds, sink, cyc), f16_flop, 2516.6, 4, false);
+  row("mfma f16, A operands from LDS", run<kLds>(iters, seconds, sink, cyc), f16_flop, 2516.6, 8, true);
+  row("mfma f16 from LDS + fma on the same SIMDs", run<kLdsFma>(iters, seconds, sink, cyc), f16_flop, 2516.6, 4, false);
+  row("mfma f16 from LDS + exp on the same SIMDs", run<kLdsExp>(iters, seconds, sink, cyc), f16_flop, 2516.6, 4, false);
   CHECK(hipFree(sink));
   CHECK(hipFree(cyc));
   return 0;

@@ -1540,9 +1540,13 @@ __device__ __forceinline__ void seq_step(WaveState<D, DT>& st, const LoopCtxT<BN
 // The sequential step over a 128-key tile (the key-tile-size axis of the
 // tuning variants): two 64-key halves share one row max, one reference
 // update and one rescale check, and each barrier hands over twice the keys.
-template <int D, int DT, bool CAUSAL, bool MASKED>
+// BS: block-scaled E4M3, one K/V block (and TileScale) per half.
+template <int D, int DT, bool CAUSAL, bool MASKED, bool BS = false>
 __device__ __forceinline__ void seq_step128(WaveState<D, DT>& st, const LoopCtxT<128>& cx, int j, const lds_t* Kc,
-                                            const lds_t* Vc) {
+                                            const lds_t* Vc, const TileScale (&ts)[2]) {
+  static_assert(!BS || DT == ATTN_FP8_E4M3, "block scales are an E4M3 variant");
+  // score scale and exponent offset of each half
+  const float c0 = BS ? ts[0].c : cx.c, c1 = BS ? ts[1].c : cx.c;
   constexpr int kRowBytes = D * Fmt<DT>::kBytes;
   constexpr int kHalf = 64 * kRowBytes;
   // The half-row-sum check of seq_step would keep all eight packed P
@@ -1566,12 +1570,13 @@ __device__ __forceinline__ void seq_step128(WaveState<D, DT>& st, const LoopCtxT
   // p in place of the scores, packed (16-bit); returns this lane's half-row
   // sum (binary16: of the rounded P; else of the unrounded p)
   auto probs = [&](float mref) -> float {
+    const float off0 = BS ? ts[0].lv - mref : -mref, off1 = BS ? ts[1].lv - mref : -mref;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], cx.c, -mref));
-      s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], cx.c, -mref));
-      s2[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], cx.c, -mref));
-      s3[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s3[r], cx.c, -mref));
+      s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c0, off0));
+      s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c0, off0));
+      s2[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], c1, off1));
+      s3[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s3[r], c1, off1));
     }
     if constexpr (DT != ATTN_FP8_E4M3) {
       pf[0] = pack8<DT>(s0, 0);
@@ -1585,6 +1590,15 @@ __device__ __forceinline__ void seq_step128(WaveState<D, DT>& st, const LoopCtxT
     }
     if constexpr (DT == ATTN_F16) {
       return row_sum_f16<8>(pf);
+    } else if constexpr (BS) {
+      // each half's p' / vd of its block
+      float la = 0.f, lb = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        la += s0[r] + s1[r];
+        lb += s2[r] + s3[r];
+      }
+      return __builtin_fmaf(la, ts[0].iv, lb * ts[1].iv);
     } else {
       float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
@@ -1603,7 +1617,8 @@ __device__ __forceinline__ void seq_step128(WaveState<D, DT>& st, const LoopCtxT
       ma = fmaxf(fmaxf(ma, s0[r]), s1[r]);
       mb = fmaxf(fmaxf(mb, s2[r]), s3[r]);
     }
-    const float m2t = swap_halves_max(fmaxf(ma, mb)) * cx.c;
+    const float m2t = BS ? swap_halves_max(fmaxf(__builtin_fmaf(ma, c0, ts[0].lv), __builtin_fmaf(mb, c1, ts[1].lv)))
+                         : swap_halves_max(fmaxf(ma, mb)) * cx.c;
     const float m2new = fmaxf(st.m2, m2t);
     const float alpha = m2new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(st.m2 - m2new);
     st.m2 = m2new;
@@ -1636,7 +1651,9 @@ __device__ __forceinline__ void seq_step128(WaveState<D, DT>& st, const LoopCtxT
       mb = fmaxf(fmaxf(mb, s2[r]), s3[r]);
     }
     bool rescale;
-    const float alpha = update_reference(st.m2, swap_halves_max(fmaxf(ma, mb)) * cx.c, rescale);
+    const float m2t = BS ? swap_halves_max(fmaxf(__builtin_fmaf(ma, c0, ts[0].lv), __builtin_fmaf(mb, c1, ts[1].lv)))
+                         : swap_halves_max(fmaxf(ma, mb)) * cx.c;
+    const float alpha = update_reference(st.m2, m2t, rescale);
     if (rescale) {
       asm volatile("" ::: "memory");  // keep the branch (see step)
       st.lrun *= alpha;
@@ -1664,7 +1681,7 @@ attn_fwd_seq_kernel(Params p) {
   constexpr int kBlockM = kWaves * kRowsPerWave;
   constexpr int kRowBytes = D * Fmt<DT>::kBytes;
   constexpr int BN = BNV ? BNV : TileKeys<D, DT>::value;
-  static_assert(!BS || BN == 64, "block-scaled tiles are one 64-row block");
+  static_assert(!BS || BN == 64 || BN == 128, "block-scaled tiles are one or two 64-row blocks");
   static_assert(DT != ATTN_FP8_E4M3 || BN == 64 || BN == 128, "E4M3 tiles are multiples of the MFMA's 64 keys");
   constexpr int kTileBytes = BN * kRowBytes;
   __shared__ __attribute__((aligned(1024))) unsigned char k_st0[kTileBytes];
@@ -1712,42 +1729,50 @@ attn_fwd_seq_kernel(Params p) {
   const int tb = min(first_bias_tile<CAUSAL>(cx), nt);
   const int jm = tb & ~1;
   // Block scales: the wave's 32 rows lie in one 64-row Q block (rows past
-  // Nq take the last block; they are not stored); K/V block j is tile j.
-  // The descales of tile j + 1 are read with that tile's loads, so the
-  // step's vmcnt wait covers them too.
-  float cq = 0.f, kd = 0.f, vd = 0.f;
+  // Nq take the last block; they are not stored); K/V blocks NB j .. NB j +
+  // NB - 1 are tile j (a block past the last one, whose keys are all
+  // masked, takes the last block's descales).  The descales of tile j + 1
+  // are read with that tile's loads, so the step's vmcnt wait covers them
+  // too.
+  constexpr int NB = BN / 64 > 0 ? BN / 64 : 1;
+  float cq = 0.f, kd[NB] = {}, vd[NB] = {};
   const float* ksh = nullptr;
   const float* vsh = nullptr;
+  auto read_scales = [&](int t) {
+#pragma unroll
+    for (int h = 0; h < NB; ++h) {
+      const int b = min(NB * t + h, p.nkb - 1);
+      kd[h] = ksh[b];
+      vd[h] = vsh[b];
+    }
+  };
   if constexpr (BS) {
     cq = p.c * p.qs[(size_t)bh * p.nqb + min(cx.qw0 / 64, p.nqb - 1)];
     ksh = p.ks + (size_t)bh * p.nkb;
     vsh = p.vs + (size_t)bh * p.nkb;
-    if (nt > 0) {
-      kd = ksh[0];
-      vd = vsh[0];
-    }
+    if (nt > 0) read_scales(0);
   }
   // Step j: K_j, V_j in (Kc, Vc); tile j + 1 -> (Kl, Vl).
   auto step = [&](int j, const lds_t* Kc, const lds_t* Vc, lds_t* Kl, lds_t* Vl, auto masked) {
     constexpr bool M = decltype(masked)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    TileScale ts{};
+    TileScale ts[NB] = {};
     if constexpr (BS) {
-      ts.c = cq * kd;
-      ts.lv = __builtin_amdgcn_logf(vd);
-      ts.iv = __builtin_amdgcn_rcpf(vd);
+#pragma unroll
+      for (int h = 0; h < NB; ++h) {
+        ts[h].c = cq * kd[h];
+        ts[h].lv = __builtin_amdgcn_logf(vd[h]);
+        ts[h].iv = __builtin_amdgcn_rcpf(vd[h]);
+      }
     }
     __syncthreads();
     if (j + 1 < nt) {
       ld.load(Kl, Kr, (j + 1) * BN);
       ld.load(Vl, Vr, (j + 1) * BN);
-      if constexpr (BS) {
-        kd = ksh[j + 1];
-        vd = vsh[j + 1];
-      }
+      if constexpr (BS) read_scales(j + 1);
     }
-    if constexpr (BN == 128) seq_step128<D, DT, CAUSAL, M>(st, cx, j, Kc, Vc);
-    else seq_step<D, DT, CAUSAL, M, BN, BS>(st, cx, j, Kc, Vc, ts);
+    if constexpr (BN == 128) seq_step128<D, DT, CAUSAL, M, BS>(st, cx, j, Kc, Vc, ts);
+    else seq_step<D, DT, CAUSAL, M, BN, BS>(st, cx, j, Kc, Vc, ts[0]);
   };
   int j = 0;
   for (; j < jm; j += 2) {
@@ -2215,8 +2240,13 @@ int launch_blockscaled(const Problem& pr, hipStream_t stream) {
   p.vs = pr.v_descales;
   p.nqb = (pr.Nq + ATTN_FP8_BLOCK_ROWS - 1) / ATTN_FP8_BLOCK_ROWS;
   p.nkb = (pr.Nk + ATTN_FP8_BLOCK_ROWS - 1) / ATTN_FP8_BLOCK_ROWS;
-  hipLaunchKernelGGL((attn_fwd_seq_kernel<D, ATTN_FP8_E4M3, CAUSAL, true>), dim3(p.total_tiles), dim3(64 * kWaves),
-                     0, stream, p);
+  // d = 128: 128-key tiles (two blocks per tile), as the per-tensor default
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((attn_fwd_seq_kernel<D, ATTN_FP8_E4M3, CAUSAL, true, 128>), dim3(p.total_tiles),
+                       dim3(64 * kWaves), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_seq_kernel<D, ATTN_FP8_E4M3, CAUSAL, true>), dim3(p.total_tiles), dim3(64 * kWaves),
+                       0, stream, p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -21,6 +21,8 @@ template __global__ void attn_fwd_seq_kernel<64, ATTN_FP8_E4M3, true>(Params);
 // Key-tile-size variant of the sequential kernel.
 template __global__ void attn_fwd_seq_kernel<64, ATTN_FP8_E4M3, false, false, 128>(Params);
 template __global__ void attn_fwd_seq_kernel<64, ATTN_FP8_E4M3, true, false, 128>(Params);
+template __global__ void attn_fwd_seq_kernel<64, ATTN_FP8_E4M3, false, true, 128>(Params);
+template __global__ void attn_fwd_seq_kernel<64, ATTN_FP8_E4M3, true, true, 128>(Params);
 
 }  // namespace kernels
 

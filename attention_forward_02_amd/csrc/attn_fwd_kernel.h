@@ -2028,10 +2028,12 @@ constexpr long long kSplitMaxGrid = 512;
 // E4M3 at d = 128 and for d = 256 (where dropping the pipelined score tile,
 // and for 16-bit inputs halving the key tile, lets two workgroups share a
 // CU, so every SIMD runs two waves: 887 -> 1,145 TFLOP/s on causal bf16),
-// the pipelined one elsewhere.
+// and for 16-bit d = 64 (its half-row-sum check keeps it at three waves per
+// SIMD: 3% faster than the pipelined kernel at B=2 H=16 N=8192, fp16 and
+// causal bf16); the pipelined one elsewhere.
 template <int D, int DT>
 struct Sequential {
-  static constexpr bool value = (D == 128 && DT == ATTN_FP8_E4M3) || D == 256;
+  static constexpr bool value = (D == 128 && DT == ATTN_FP8_E4M3) || D == 256 || (D == 64 && DT != ATTN_FP8_E4M3);
 };
 
 // binary16 at d = 128 takes the producer-wave kernel: 1.8-3.5% faster than
@@ -2045,7 +2047,10 @@ struct UseProducer {
 // E4M3 at d = 128 takes the sequential kernel with 128-key tiles: its step
 // is bound by softmax VALU work, and one row max, reference update and
 // barrier per 128 keys instead of per 64 measured 5% faster than 64-key
-// tiles on B=2 H=16 N=8192 with outliers (0.557 vs 0.585 ms).
+// tiles on B=2 H=16 N=8192 with outliers (0.557 vs 0.585 ms).  (At d = 64
+// it is 5% faster than the pipelined kernel too, 0.388 vs 0.409 ms, but it
+// misses the E4M3 gate on a one-row edge case the pipelined kernel meets,
+// so d = 64 keeps that one.)
 template <int D, int DT>
 struct UseBC128 {
   static constexpr bool value = D == 128 && DT == ATTN_FP8_E4M3;
@@ -2240,8 +2245,8 @@ int launch_blockscaled(const Problem& pr, hipStream_t stream) {
   p.vs = pr.v_descales;
   p.nqb = (pr.Nq + ATTN_FP8_BLOCK_ROWS - 1) / ATTN_FP8_BLOCK_ROWS;
   p.nkb = (pr.Nk + ATTN_FP8_BLOCK_ROWS - 1) / ATTN_FP8_BLOCK_ROWS;
-  // d = 128: 128-key tiles (two blocks per tile), as the per-tensor default
-  if constexpr (D == 128)
+  // d = 64, 128: 128-key tiles (two blocks per tile), as the per-tensor default
+  if constexpr (D != 256)
     hipLaunchKernelGGL((attn_fwd_seq_kernel<D, ATTN_FP8_E4M3, CAUSAL, true, 128>), dim3(p.total_tiles),
                        dim3(64 * kWaves), 0, stream, p);
   else

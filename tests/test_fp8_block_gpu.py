@@ -121,6 +121,41 @@ def test_blockscaled_forward(d, causal, nq, nk, outliers):
     say(f"[gpu] {label}: {stats}")
 
 
+@pytest.mark.parametrize("nk", [300, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_blockscaled_unequal_block_scales(d, causal, nk):
+    """K and V blocks of very different magnitudes (odd 64-row blocks: K x3,
+    V x1/8), so the descales of the two 64-key halves of a 128-key tile
+    differ by large factors and the larger scores sit in the second half:
+    a half scored or weighted with the other half's descales, or a row max
+    that misses one half, misses the gates by far."""
+    label = f"blockscaled unequal block scales d={d} causal={causal} Nk={nk}"
+    say(f"[gpu] {label}: B=1 H=2 Nq=200")
+    inp = inputs.make(1, 2, 200, nk, d, "f16", seed=300 + d + nk)
+    x = [oracle.decode_f16(t) for t in (inp.q, inp.k, inp.v)]
+    odd = (np.arange(nk) // 64) % 2 == 1
+    x[1][:, :, odd, :] *= 3.0
+    x[2][:, :, odd, :] *= 0.125
+    (qc, qd), (kc, kd), (vc, vd) = (oracle.quantize_blocks(t, had) for t, had in zip(x, (True, True, False)))
+    assert kd[0, 0, 1] > 2.0 * kd[0, 0, 0] and vd[0, 0, 1] < 0.25 * vd[0, 0, 0]
+    dev = torch.device("cuda:0")
+    up8 = lambda c: torch.from_numpy(c).to(dev)
+    upf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    o, lse = attention_fp8_blockscaled(up8(qc), up8(kc), up8(vc), upf(qd), upf(kd), upf(vd), causal=causal,
+                                       scale=float(inp.scale))
+    torch.cuda.synchronize()
+    qq, kk, vv = (oracle.dequantize_blocks(c, sc) for c, sc in ((qc, qd), (kc, kd), (vc, vd)))
+    o_ref, lse_ref = oracle.attention(qq, kk, vv, causal, float(inp.scale))
+    # O at the stated E4M3 gate; LSE against a coarse bound only (larger
+    # logits enlarge the E4M3 matrix core's own rounding), which a half with
+    # the wrong descales (off by ln 3 or more in its scores) still misses.
+    stats = compare(o.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy(), o_ref, lse_ref, "e4m3",
+                    label, lse_gate=False)
+    say(f"[gpu] {label}: {stats}")
+    assert stats["max_abs_dLSE"] <= 5e-2, f"{label}: max |dLSE| {stats['max_abs_dLSE']:.3g}"
+
+
 def test_blockscaled_equals_per_tensor_when_scales_agree():
     # One power-of-two descale per tensor, repeated for every block: both
     # kernels then scale by exact powers of two and must agree up to the E4M3

@@ -2059,9 +2059,10 @@ struct UseBC128 {
 // Kernel choices a caller can make (include/attn.h, attn_fwd_variant):
 // the pipelined kernel with a two- or four-stage ring (not at d = 256, whose
 // pipelined registers leave one wave per SIMD), the sequential kernel, the
-// split-key kernel (16-bit d = 64), the pingpong kernel (16-bit d = 128) and
-// the producer-wave kernel (d = 128).  ATTN_VARIANT_AUTO takes the measured
-// defaults above.
+// split-key kernel (16-bit d = 64), the pingpong kernel (d = 128), the
+// producer-wave kernel (d = 128), the wide-wave kernel (16-bit d = 128), the
+// sequential kernel with 32- or 128-key tiles and the three-stage pipelined
+// kernel.  ATTN_VARIANT_AUTO takes the measured defaults above.
 template <int D, int DT>
 struct Variants {
   static constexpr bool pipelined = D != 256;

@@ -18,6 +18,7 @@
 //   fma        waves 0-3 only (one wave per SIMD): 16 independent fp32 FMA
 //              chains, 32 FMAs per iteration
 //   exp        waves 0-3 only: 16 v_exp_f32 (+ 16 multiplies) per iteration
+//   exp alone  waves 0-3 only: 16 v_exp_f32 per iteration, nothing else
 //   mfma f16 + fma / + exp: waves 0-3 the f16 MFMA loop, waves 4-7 (same
 //              SIMDs) the fma or exp loop at the same time
 //   mfma f16 + lds (+ fma / + exp): the MFMA waves take their A operands
@@ -41,7 +42,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-enum { kMfmaF16 = 0, kMfmaFp8 = 1, kFma = 2, kExp = 3, kMfmaFma = 4, kMfmaExp = 5, kLds = 6, kLdsFma = 7, kLdsExp = 8 };
+enum { kMfmaF16 = 0, kMfmaFp8 = 1, kFma = 2, kExp = 3, kMfmaFma = 4, kMfmaExp = 5, kLds = 6, kLdsFma = 7, kLdsExp = 8,
+       kExpOnly = 9 };
 constexpr int kCUs = 256;
 constexpr int kWaves = 8;
 
@@ -52,7 +54,7 @@ __global__ void __launch_bounds__(512) ceiling_kernel(float* sink, long long* cy
   constexpr bool kUsesLds = T == kLds || T == kLdsFma || T == kLdsExp;
   constexpr bool kExpLoop = T == kExp || T == kMfmaExp || T == kLdsExp;
   const bool mfma_wave = (T == kMfmaF16 || T == kMfmaFp8 || T == kLds) || (kPair && w < 4);
-  const bool valu_wave = ((T == kFma || T == kExp) && w < 4) || (kPair && w >= 4);
+  const bool valu_wave = ((T == kFma || T == kExp || T == kExpOnly) && w < 4) || (kPair && w >= 4);
   constexpr int kLdsBytes = 16384;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kUsesLds ? kLdsBytes : 16];
   if constexpr (kUsesLds) {
@@ -130,7 +132,9 @@ __global__ void __launch_bounds__(512) ceiling_kernel(float* sink, long long* cy
     for (int it = 0; it < n; ++it) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if constexpr (!kExpLoop) {
+        if constexpr (T == kExpOnly) {
+          x[i] = __builtin_amdgcn_exp2f(-x[i]);  // stays in (0, 1]; the sign is a free operand modifier
+        } else if constexpr (!kExpLoop) {
           x[i] = __builtin_fmaf(x[i], 0.999f, 0.001f);
           x[i] = __builtin_fmaf(x[i], 0.999f, 0.001f);
         } else {
@@ -187,7 +191,7 @@ Result run(int iters, double seconds, float* sink, long long* cyc) {
   std::vector<long long> c(kCUs * kWaves);
   CHECK(hipMemcpy(c.data(), cyc, c.size() * sizeof(long long), hipMemcpyDeviceToHost));
   const bool both = T == kMfmaFma || T == kMfmaExp || T == kLdsFma || T == kLdsExp;
-  const bool valu_only = T == kFma || T == kExp;
+  const bool valu_only = T == kFma || T == kExp || T == kExpOnly;
   double mc = 0, vc = 0, maxc = 0;
   for (int b = 0; b < kCUs; ++b)
     for (int w = 0; w < kWaves; ++w) {
@@ -247,6 +251,7 @@ int main(int argc, char** argv) {
   row("mfma fp8 (4 x 32x32x64 per iteration)", run<kMfmaFp8>(iters, seconds, sink, cyc), fp8_flop, 5033.2, 8, true);
   row("fma (32 per iteration)", run<kFma>(iters, seconds, sink, cyc), 0, 0, 0, false);
   row("exp (16 exp + 16 mul per iteration)", run<kExp>(iters, seconds, sink, cyc), 0, 0, 0, false);
+  row("exp alone (16 per iteration)", run<kExpOnly>(iters, seconds, sink, cyc), 0, 0, 0, false);
   row("mfma f16 + fma on the same SIMDs", run<kMfmaFma>(iters, seconds, sink, cyc), f16_flop, 2516.6, 4, false);
   row("mfma f16 + exp on the same SIMDs", run<kMfmaExp>(iters, seconds, sink, cyc), f16_flop, 2516.6, 4, false);
   row("mfma f16, A operands from LDS", run<kLds>(iters, seconds, sink, cyc), f16_flop, 2516.6, 8, true);

@@ -2,6 +2,10 @@
 attention shape on the GPU and list them fastest first.
 
     python -m attention_forward_02_amd.tune --workload hd128_seq8k_f16 [--reps 20] [--write]
+    python -m attention_forward_02_amd.tune --shape 2,16,8192,8192,64,bf16,causal
+
+(--shape B,H,Nq,Nk,d,dtype[,causal]: seeded N(0, 1) inputs of that shape,
+the way the named workloads are drawn, for a shape of one's own.)
 
 The variants (ATTN_VARIANT_* in include/attn.h) compute the same forward pass
 with different schedules: the pipelined kernel with a two- or four-stage K/V
@@ -134,6 +138,7 @@ def _table(rows, workload, cmd):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--workload", default="hd128_seq8k_f16")
+    ap.add_argument("--shape", help="B,H,Nq,Nk,d,dtype[,causal] instead of a named workload")
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--rounds", type=int, default=3)
     ap.add_argument("--write", action="store_true", help="write profiles/tuning_<workload>.md")
@@ -141,10 +146,18 @@ def main(argv=None):
     import numpy as np
     import torch
     from . import inputs
-    w = inputs.WORKLOADS[args.workload]
-    if w.get("smoothed"):
-        sys.exit("the block-scaled path has a single kernel variant")
-    inp = inputs.make_workload(args.workload)
+    if args.shape:
+        f = args.shape.split(",")
+        if len(f) not in (6, 7) or (len(f) == 7 and f[6] != "causal"):
+            sys.exit("--shape takes B,H,Nq,Nk,d,dtype[,causal]")
+        B, H, Nq, Nk, d = (int(x) for x in f[:5])
+        inp = inputs.make(B, H, Nq, Nk, d, f[5], seed=1, causal=len(f) == 7)
+        label = args.shape
+    else:
+        if inputs.WORKLOADS[args.workload].get("smoothed"):
+            sys.exit("the block-scaled path has a single kernel variant")
+        inp = inputs.make_workload(args.workload)
+        label = args.workload
     dev = torch.device("cuda:0")
     if inp.dtype == "e4m3":
         up = lambda x: torch.from_numpy(x).view(torch.float8_e4m3fn).to(dev)
@@ -155,12 +168,13 @@ def main(argv=None):
         desc = None
     rows = tune(up(inp.q), up(inp.k), up(inp.v), inp.causal, float(inp.scale), desc, reps=args.reps,
                 rounds=args.rounds)
-    cmd = (f"python -m attention_forward_02_amd.tune --workload {args.workload} --reps {args.reps} "
-           f"--rounds {args.rounds} --write")
-    text = _table(rows, args.workload, cmd)
+    which = f"--shape {args.shape}" if args.shape else f"--workload {args.workload}"
+    cmd = f"python -m attention_forward_02_amd.tune {which} --reps {args.reps} --rounds {args.rounds} --write"
+    text = _table(rows, label, cmd)
     print(text, flush=True)
     if args.write:
-        with open(os.path.join(ROOT, "profiles", f"tuning_{args.workload}.md"), "w") as f:
+        name = args.workload if not args.shape else "shape_" + args.shape.replace(",", "_")
+        with open(os.path.join(ROOT, "profiles", f"tuning_{name}.md"), "w") as f:
             f.write(text)
 
 

@@ -175,8 +175,18 @@ __device__ __forceinline__ uint32_t pack16(float x, float y) {
 
 // Four floats -> four E4M3 bytes, in order (v_cvt_pk_fp8_f32 twice, RNE).
 // Inputs here are probabilities in [0, 2^8], inside E4M3's finite range.
+// The first conversion writes the low half of the word and the second the
+// high half, so the word's previous contents never matter.  The builtin
+// takes them as an operand (and the compiler then clears the word with a
+// v_mov first); with kAsm the first conversion is written out instead,
+// leaving the high half as it finds it until the second one overwrites it.
+// The pipelined step keeps the builtin: its instruction interleave counts
+// VALU instructions, and an asm statement is not one to the scheduler.
+template <bool kAsm = true>
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int lo;
+  if constexpr (kAsm) asm("v_cvt_pk_fp8_f32 %0, %1, %2" : "=v"(lo) : "v"(a), "v"(b));
+  else lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
@@ -562,12 +572,13 @@ __device__ __forceinline__ float row_sum_f16(const i16x8 (&pf)[NPF]) {
 
 // P^T as the E4M3 B operand of the P V MFMA: byte 16s + r holds element r
 // of the tile's s-th score accumulator.
+template <bool kAsm = true>
 __device__ __forceinline__ i32x8 pack_p_fp8(const f32x16& p0, const f32x16& p1) {
   i32x8 r;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    r[w] = pack_fp8x4(p0[4 * w], p0[4 * w + 1], p0[4 * w + 2], p0[4 * w + 3]);
-    r[w + 4] = pack_fp8x4(p1[4 * w], p1[4 * w + 1], p1[4 * w + 2], p1[4 * w + 3]);
+    r[w] = pack_fp8x4<kAsm>(p0[4 * w], p0[4 * w + 1], p0[4 * w + 2], p0[4 * w + 3]);
+    r[w + 4] = pack_fp8x4<kAsm>(p1[4 * w], p1[4 * w + 1], p1[4 * w + 2], p1[4 * w + 3]);
   }
   return r;
 }
@@ -699,7 +710,7 @@ __device__ __forceinline__ void step(WaveState<D, DT>& st, const LoopCtx& cx, in
   }
   if constexpr (DT == ATTN_FP8_E4M3) {
     // D/32 MFMAs of 64 cycles per phase; two 16-byte K reads per MFMA.
-    const i32x8 pf = pack_p_fp8(s0, s1);
+    const i32x8 pf = pack_p_fp8<false>(s0, s1);
     if constexpr (D == 64) ATTN_INTERLEAVE(2, 2, 40, 2);
     else if constexpr (D == 128) ATTN_INTERLEAVE(2, 4, 20, 2);
     else ATTN_INTERLEAVE(2, 8, 10, 2);

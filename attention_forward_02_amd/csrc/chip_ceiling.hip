@@ -29,6 +29,21 @@
 //
 // The MFMA operands are distinct per lane and the accumulators feed back,
 // so no iteration can be folded away.
+//
+// A second table models one step of the attention kernels per wave, with
+// the step's dependences: S = A B (8 chained 32x32x16 f16 MFMAs, B the
+// previous iteration's P), p = exp2(c S - m) (16 FMAs, 16 exp2, 8 packs to
+// binary16), O += A' P (8 MFMAs over 4 accumulators): 512 MFMA cycles and
+// about 300 VALU cycles per iteration.  It runs with one or two waves per
+// SIMD, with the A operands in registers or read from LDS one 16-byte read
+// per MFMA (the P V operands optionally by two ds_read_b64_tr_b16, as the
+// kernels read V), and optionally with a workgroup barrier per iteration.
+// Matrix-core use = 512 cycles x waves per SIMD over the slowest wave's
+// cycles per iteration.
+//
+// A third table gives the CU's LDS read rate: every wave issues `n` reads
+// (ds_read_b128 or ds_read_b64_tr_b16, conflict-free addresses), waits for
+// them, and repeats.
 #include <hip/hip_runtime.h>
 
 #include <chrono>
@@ -149,6 +164,108 @@ __global__ void __launch_bounds__(512) ceiling_kernel(float* sink, long long* cy
   if (lane == 0) cycles[blockIdx.x * kWaves + w] = t1 - t0;
 }
 
+// One attention-like step per iteration (see the header).  MODE bits:
+// 1 = barrier per iteration, 2 = A operands from LDS, 4 = P V operands by
+// transpose reads (with 2).
+template <int MODE>
+__global__ void __launch_bounds__(512) step_kernel(const f16x8* ain, float* sink, long long* cycles, int iters,
+                                                   float c, float m) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef _Float16 lds_f16x8 __attribute__((ext_vector_type(8), address_space(3)));
+  typedef short lds_i16x4 __attribute__((ext_vector_type(4), address_space(3)));
+  __shared__ __attribute__((aligned(1024))) _Float16 lds[8192];  // 16 KB: 1024 16-byte operands
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < 8192; i += blockDim.x) lds[i] = (_Float16)(0.001f * ((i * 37) % 97));
+  __syncthreads();
+  f16x8 a[8], pf[2];
+  for (int k = 0; k < 8; ++k) a[k] = ain[lane + 64 * k];
+  for (int i = 0; i < 8; ++i) {
+    pf[0][i] = (_Float16)0.5f;
+    pf[1][i] = (_Float16)0.25f;
+  }
+  f32x16 o[4] = {};
+  const lds_f16x8* L = (const lds_f16x8*)lds;
+  const long long t0 = __builtin_readcyclecounter();
+#pragma nounroll
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (MODE & 1) __syncthreads();
+    f32x16 s = {};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const f16x8 av = (MODE & 2) ? L[(lane + 64 * k + 7 * it) & 1023] : a[k];
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pf[k & 1], s, 0, 0, 0);
+    }
+    float pr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 t = __builtin_convertvector((f32x2){pr[8 * h + 2 * e], pr[8 * h + 2 * e + 1]}, f16x2);
+        pf[h][2 * e] = t[0];
+        pf[h][2 * e + 1] = t[1];
+      }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      f16x8 av;
+      const int idx = (lane + 64 * (k + 8) + 5 * it) & 1023;
+      if constexpr ((MODE & 6) == 6) {
+        const __attribute__((address_space(3))) char* base = (const __attribute__((address_space(3))) char*)lds;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * idx));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + ((16 * idx) ^ 8)));
+        av = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {
+        av = (MODE & 2) ? L[idx] : a[k];
+      }
+      o[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pf[k & 1], o[k & 3], 0, 0, 0);
+    }
+  }
+  const long long t1 = __builtin_readcyclecounter();
+  float acc = 0.f;
+  for (int j = 0; j < 4; ++j)
+    for (int i = 0; i < 16; ++i) acc += o[j][i];
+  sink[blockIdx.x * 512 + threadIdx.x] = acc;
+  if (lane == 0) cycles[blockIdx.x * kWaves + w] = t1 - t0;
+}
+
+// LDS read rate: n reads in flight per wave, then a wait; TR: the
+// transpose read instead of ds_read_b128.
+template <bool TR, int N>
+__global__ void __launch_bounds__(1024) lds_kernel(float* sink, long long* cycles, int iters) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef int lds_i32x4 __attribute__((ext_vector_type(4), address_space(3)));
+  typedef short lds_i16x4 __attribute__((ext_vector_type(4), address_space(3)));
+  __shared__ __attribute__((aligned(1024))) int lds[16384];  // 64 KB
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < 16384; i += blockDim.x) lds[i] = i * 40503;
+  __syncthreads();
+  const __attribute__((address_space(3))) char* base = (const __attribute__((address_space(3))) char*)lds;
+  const long long t0 = __builtin_readcyclecounter();
+#pragma nounroll
+  for (int it = 0; it < iters; ++it) {
+    i32x4 x[N];
+    i16x4 y[N];
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+      const int idx = (lane + 64 * ((r + it) & 15) + 1024 * (w & 3)) & 4095;  // 16-byte units
+      if constexpr (TR) y[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * idx));
+      else x[r] = *(const lds_i32x4*)(base + 16 * idx);
+    }
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+      if constexpr (TR) asm volatile("" ::"v"(y[r]));
+      else asm volatile("" ::"v"(x[r]));
+    }
+  }
+  const long long t1 = __builtin_readcyclecounter();
+  sink[blockIdx.x * 1024 + threadIdx.x] = 0.f;
+  if (lane == 0) cycles[blockIdx.x * 16 + w] = t1 - t0;
+}
+
 struct Result {
   double ms_per_launch, mfma_cycles_per_iter, valu_cycles_per_iter, clock_ghz;
 };
@@ -213,6 +330,75 @@ Result run(int iters, double seconds, float* sink, long long* cyc) {
   return r;
 }
 
+// Settle for `seconds` of launches, then time `seconds` more; returns ms
+// per launch.
+template <typename F>
+double timed(F launch, double seconds) {
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  const auto start = std::chrono::steady_clock::now();
+  while (std::chrono::duration<double>(std::chrono::steady_clock::now() - start).count() < seconds) {
+    launch();
+    CHECK(hipDeviceSynchronize());
+  }
+  int n = 0;
+  float total_ms = 0.f;
+  while (total_ms < seconds * 1e3f) {
+    CHECK(hipEventRecord(e0));
+    launch();
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    float ms;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    total_ms += ms;
+    ++n;
+  }
+  CHECK(hipGetLastError());
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+  return total_ms / n;
+}
+
+// Largest per-wave cycle count of the last launch (waves < W of each block;
+// `stride` entries per block).
+double slowest(const long long* cyc, int W, int stride) {
+  std::vector<long long> c((size_t)kCUs * stride);
+  CHECK(hipMemcpy(c.data(), cyc, c.size() * sizeof(long long), hipMemcpyDeviceToHost));
+  long long mx = 0;
+  for (int b = 0; b < kCUs; ++b)
+    for (int w = 0; w < W; ++w) mx = c[(size_t)b * stride + w] > mx ? c[(size_t)b * stride + w] : mx;
+  return (double)mx;
+}
+
+template <int MODE>
+void step_row(const char* name, int W, const f16x8* ain, float* sink, long long* cyc, double seconds) {
+  const int iters = 4000;
+  CHECK(hipMemset(cyc, 0, (size_t)kCUs * kWaves * sizeof(long long)));
+  const double ms = timed(
+      [&]() {
+        hipLaunchKernelGGL((step_kernel<MODE>), dim3(kCUs), dim3(64 * W), 0, 0, ain, sink, cyc, iters, 0.05f, 1.0f);
+      },
+      seconds);
+  const double per_iter = slowest(cyc, W, kWaves) / iters;
+  const double use = 512.0 * (W / 4) / per_iter;
+  std::printf("| %s | %d | %.1f | %.0f%% | %.2f |\n", name, W / 4, per_iter, 100.0 * use,
+              slowest(cyc, W, kWaves) / (ms * 1e-3) / 1e9);
+  std::fflush(stdout);
+}
+
+template <bool TR, int N>
+void lds_row(int W, float* sink, long long* cyc, double seconds) {
+  const int iters = 20000;
+  CHECK(hipMemset(cyc, 0, (size_t)kCUs * 16 * sizeof(long long)));
+  timed([&]() { hipLaunchKernelGGL((lds_kernel<TR, N>), dim3(kCUs), dim3(64 * W), 0, 0, sink, cyc, iters); },
+        seconds);
+  const double bytes = (double)W * iters * N * 64 * (TR ? 8 : 16);
+  std::printf("| %s | %d | %d | %.0f |\n", TR ? "ds_read_b64_tr_b16" : "ds_read_b128", W, N,
+              bytes / slowest(cyc, W, 16));
+  std::fflush(stdout);
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -257,6 +443,38 @@ int main(int argc, char** argv) {
   row("mfma f16, A operands from LDS", run<kLds>(iters, seconds, sink, cyc), f16_flop, 2516.6, 8, true);
   row("mfma f16 from LDS + fma on the same SIMDs", run<kLdsFma>(iters, seconds, sink, cyc), f16_flop, 2516.6, 4, false);
   row("mfma f16 from LDS + exp on the same SIMDs", run<kLdsExp>(iters, seconds, sink, cyc), f16_flop, 2516.6, 4, false);
+  CHECK(hipFree(sink));
+  CHECK(hipFree(cyc));
+
+  // Step model and LDS rates: buffers sized for 16 waves per block.
+  CHECK(hipMalloc(&sink, (size_t)kCUs * 1024 * sizeof(float)));
+  CHECK(hipMalloc(&cyc, (size_t)kCUs * 16 * sizeof(long long)));
+  f16x8* ain;
+  CHECK(hipMalloc(&ain, 512 * sizeof(f16x8)));
+  {
+    std::vector<_Float16> h(512 * 8);
+    for (size_t i = 0; i < h.size(); ++i) h[i] = (_Float16)(0.01f + 0.0001f * (float)((i * 7) % 50));
+    CHECK(hipMemcpy(ain, h.data(), h.size() * sizeof(_Float16), hipMemcpyHostToDevice));
+  }
+  std::printf("\n| step model (4,000 iterations per wave) | waves per SIMD | cycles / iteration (slowest wave) | "
+              "matrix-core use | shader clock (GHz) |\n|---|---|---|---|---|\n");
+  step_row<0>("operands in registers", 4, ain, sink, cyc, seconds);
+  step_row<0>("operands in registers", 8, ain, sink, cyc, seconds);
+  step_row<1>("operands in registers, barrier per iteration", 8, ain, sink, cyc, seconds);
+  step_row<2>("operands from LDS", 4, ain, sink, cyc, seconds);
+  step_row<2>("operands from LDS", 8, ain, sink, cyc, seconds);
+  step_row<3>("operands from LDS, barrier per iteration", 8, ain, sink, cyc, seconds);
+  step_row<7>("operands from LDS, P V operands by transpose reads, barrier per iteration", 8, ain, sink, cyc,
+              seconds);
+  std::printf("\n| LDS read | waves per CU | reads in flight per wave | bytes per clock per CU |\n|---|---|---|---|\n");
+  lds_row<false, 2>(8, sink, cyc, seconds);
+  lds_row<false, 4>(8, sink, cyc, seconds);
+  lds_row<false, 16>(8, sink, cyc, seconds);
+  lds_row<false, 16>(16, sink, cyc, seconds);
+  lds_row<true, 4>(8, sink, cyc, seconds);
+  lds_row<true, 16>(8, sink, cyc, seconds);
+  lds_row<true, 16>(16, sink, cyc, seconds);
+  CHECK(hipFree(ain));
   CHECK(hipFree(sink));
   CHECK(hipFree(cyc));
   return 0;

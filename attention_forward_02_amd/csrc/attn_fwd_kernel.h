@@ -570,6 +570,24 @@ __device__ __forceinline__ float row_sum_f16(const i16x8 (&pf)[NPF]) {
   return (l[0] + l[1]) + (l[2] + l[3]);
 }
 
+// The same sum added straight into acc as one v_dot2 chain: no zeroed
+// partial sums to start and no adds to join them (a wave64 VALU
+// instruction takes four cycles, so the chain's dependences cost nothing).
+template <int NP, int NPF>
+__device__ __forceinline__ float row_sum_f16_into(const i16x8 (&pf)[NPF], float acc) {
+  static_assert(NP <= NPF, "fragments to sum");
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const u32x4 w = __builtin_bit_cast(u32x4, pf[i]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t we = w[e];
+      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, we), (f16x2){(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+    }
+  }
+  return acc;
+}
+
 // P^T as the E4M3 B operand of the P V MFMA: byte 16s + r holds element r
 // of the tile's s-th score accumulator.
 template <bool kAsm = true>
@@ -1451,7 +1469,7 @@ __device__ __forceinline__ void seq_step(WaveState<D, DT>& st, const LoopCtxT<BN
       }
       pv_tile<D, DT, BN>(st, pf, Vc);
       if constexpr (DT == ATTN_F16) {
-        st.lrun += row_sum_f16<BN / 16>(pf);
+        st.lrun = row_sum_f16_into<BN / 16>(pf, st.lrun);
         return;
       }
     }

@@ -679,6 +679,24 @@ __device__ __forceinline__ void masked_scores(const WaveState<D, DT>& st, const 
 }
 
 // Reference update from a tile's row max (in units of scale*log2(e)):
+// raise m2 only when some row's max exceeds it by more than kLazy, and
+// rescale O and l by 2^(old - new) then.  Only the test runs on every tile;
+// the rest sits in a wave-uniform, rarely taken branch.
+template <int D, int DT>
+__device__ __forceinline__ void lazy_rescale(WaveState<D, DT>& st, float m2t) {
+  if (__any(m2t > st.m2 + kLazy)) {
+    // The empty asm keeps this block a real branch (see step).
+    asm volatile("" ::: "memory");
+    const float m2new = fmaxf(st.m2, m2t);
+    const float alpha = (m2new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(st.m2 - m2new);
+    st.m2 = m2new;
+    st.lrun *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha;
+  }
+}
+
+// Reference update from a tile's row max (in units of scale*log2(e)):
 // raise m2 only when some row's max exceeds it by more than kLazy.  Returns
 // the factor O and l must be multiplied by, 1 when nothing changed.
 __device__ __forceinline__ float update_reference(float& m2, float m2t, bool& rescale) {
@@ -1442,14 +1460,7 @@ __device__ __forceinline__ void seq_step(WaveState<D, DT>& st, const LoopCtxT<BN
   if constexpr (!SUMCHECK) {
     float m2t = tile_max2<BN>(s0, s1, c);
     if constexpr (BS) m2t += ts.lv;
-    bool rescale;
-    const float alpha = update_reference(st.m2, m2t, rescale);
-    if (rescale) {
-      asm volatile("" ::: "memory");  // keep the branch (see step)
-      st.lrun *= alpha;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha;
-    }
+    lazy_rescale<D, DT>(st, m2t);
     const float mref = (st.m2 == -__builtin_inff()) ? 0.f : st.m2;
     const float off = BS ? ts.lv - mref : -mref;
 #pragma unroll
@@ -1679,16 +1690,9 @@ __device__ __forceinline__ void seq_step128(WaveState<D, DT>& st, const LoopCtxT
       ma = fmaxf(fmaxf(ma, s0[r]), s1[r]);
       mb = fmaxf(fmaxf(mb, s2[r]), s3[r]);
     }
-    bool rescale;
     const float m2t = BS ? swap_halves_max(fmaxf(__builtin_fmaf(ma, c0, ts[0].lv), __builtin_fmaf(mb, c1, ts[1].lv)))
                          : swap_halves_max(fmaxf(ma, mb)) * cx.c;
-    const float alpha = update_reference(st.m2, m2t, rescale);
-    if (rescale) {
-      asm volatile("" ::: "memory");  // keep the branch (see step)
-      st.lrun *= alpha;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) st.oacc[i] *= alpha;
-    }
+    lazy_rescale<D, DT>(st, m2t);
     ls = probs(st.m2 == -__builtin_inff() ? 0.f : st.m2);
   }
   if constexpr (DT == ATTN_FP8_E4M3) {

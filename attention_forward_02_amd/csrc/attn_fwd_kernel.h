@@ -2047,15 +2047,27 @@ __global__ void __launch_bounds__(512) attn_fwd_split_kernel(Params p) {
   }
 }
 
-// The split-key kernel is available for 16-bit d = 64 and used for grids of
-// kSplitMinGrid to kSplitMaxGrid 128-row query tiles (a grid of a few tiles
-// is bound by launch and load latency, which the split does not shorten).
+// 16-bit d = 64 on grids of kSplitMinGrid to kSplitMaxGrid 128-row query
+// tiles (a grid of a few tiles is bound by launch and load latency, a grid
+// of more than two rounds of the 256 CUs by throughput): the split-key
+// kernel where the longest key loops are the critical path -- up to one
+// round of tiles with at least kSplitMinKeys keys, or causal with at least
+// kSplitMinKeysCausal keys on up to two rounds -- and the sequential kernel
+// with 128-key tiles (two 4-wave workgroups per CU) otherwise.  Tuner runs
+// over 20 shapes in this range put each choice ahead of the other by 1-35%,
+// except at 64 tiles with 1,024 keys, where the two are within 2%.
 template <int D, int DT>
 struct UseSplit {
   static constexpr bool value = (D == 64 && DT != ATTN_FP8_E4M3);
 };
 constexpr long long kSplitMinGrid = 64;
 constexpr long long kSplitMaxGrid = 512;
+constexpr int kSplitMinKeys = 2048;
+constexpr int kSplitMinKeysCausal = 4096;
+__host__ inline bool split_wins(long long grid128, int Nk, bool causal) {
+  if (grid128 <= 256) return Nk >= kSplitMinKeys;
+  return causal && Nk >= kSplitMinKeysCausal;
+}
 
 // Which loop a (head dim, format) uses: the sequential-step kernel for
 // E4M3 at d = 128 and for d = 256 (where dropping the pipelined score tile,
@@ -2166,10 +2178,9 @@ int launch_one(const Problem& pr, hipStream_t stream) {
     variant = Sequential<D, DT>::value ? ATTN_VARIANT_SEQUENTIAL : ATTN_VARIANT_PIPELINED;
     if (UseProducer<D, DT>::value) variant = ATTN_VARIANT_PRODUCER;
     if (UseBC128<D, DT>::value) variant = ATTN_VARIANT_SEQUENTIAL_BC128;
-    // Split-key kernel while 128-row query tiles do not fill two rounds of
-    // the 256 CUs (and there are enough of them to be worth splitting).
+    // Mid-size 16-bit d = 64 grids: split-key or 128-key sequential kernel.
     if (UseSplit<D, DT>::value && grid128 >= kSplitMinGrid && grid128 <= kSplitMaxGrid)
-      variant = ATTN_VARIANT_SPLIT;
+      variant = split_wins(grid128, pr.Nk, CAUSAL) ? ATTN_VARIANT_SPLIT : ATTN_VARIANT_SEQUENTIAL_BC128;
   }
   const dim3 block(64 * kWaves);
   switch (variant) {

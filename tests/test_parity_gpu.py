@@ -117,18 +117,28 @@ def test_nonpositive_scale(scale, causal, d, dtype):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_d64_split_key_grid(causal, dtype):
-    """d = 64 with 64..512 query tiles of 128 rows and a ragged N: the
-    split-key kernel (two groups walk the two halves of the keys and merge)."""
-    inp = inputs.make(4, 16, 300, 300, 64, dtype, seed=4343 + int(causal), causal=causal)
+    """d = 64 with 64..256 query tiles of 128 rows and a long, ragged key
+    range (at least 2,048 keys): the split-key kernel (two groups walk the
+    two halves of the keys and merge)."""
+    inp = inputs.make(2, 16, 300, 2100, 64, dtype, seed=4343 + int(causal), causal=causal)
     _full_check(inp, f"d64 split-key {'causal' if causal else 'full'} {dtype}")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
+def test_d64_mid_grid_short_keys(causal, dtype):
+    """d = 64 with 64..512 query tiles of 128 rows and a short, ragged key
+    range: the sequential kernel with 128-key tiles."""
+    inp = inputs.make(4, 16, 300, 300, 64, dtype, seed=4545 + int(causal), causal=causal)
+    _full_check(inp, f"d64 mid grid, 128-key tiles {'causal' if causal else 'full'} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
 def test_d64_large_grid(causal, dtype):
-    """d = 64 with more than 512 query tiles of 128 rows: the regular kernel,
-    as for grids of fewer than 64 tiles (the edge shapes); 64..512 tiles take
-    the split-key kernel."""
+    """d = 64 with more than 512 query tiles of 128 rows: the sequential
+    kernel with 64-key tiles, as for grids of fewer than 64 tiles (the edge
+    shapes)."""
     inp = inputs.make(2, 17, 2000, 2000, 64, dtype, seed=4242 + int(causal), causal=causal)
     _full_check(inp, f"d64 large grid {'causal' if causal else 'full'} {dtype}")
 

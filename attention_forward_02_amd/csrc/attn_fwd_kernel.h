@@ -1766,11 +1766,15 @@ attn_fwd_seq_kernel(Params p) {
   // NB - 1 are tile j (a block past the last one, whose keys are all
   // masked, takes the last block's descales).  The descales of tile j + 1
   // are read with that tile's loads, so the step's vmcnt wait covers them
-  // too.
+  // too.  The pointers are global-address-space ones: through a generic
+  // pointer the reads become flat loads, which the compiler must order
+  // after the tile's direct-to-LDS loads (a flat address may be LDS), so it
+  // waits for those loads right after issuing them.
   constexpr int NB = BN / 64 > 0 ? BN / 64 : 1;
   float cq = 0.f, kd[NB] = {}, vd[NB] = {};
-  const float* ksh = nullptr;
-  const float* vsh = nullptr;
+  typedef const __attribute__((address_space(1))) float gfloat;
+  gfloat* ksh = nullptr;
+  gfloat* vsh = nullptr;
   auto read_scales = [&](int t) {
 #pragma unroll
     for (int h = 0; h < NB; ++h) {
@@ -1780,9 +1784,9 @@ attn_fwd_seq_kernel(Params p) {
     }
   };
   if constexpr (BS) {
-    cq = p.c * p.qs[(size_t)bh * p.nqb + min(cx.qw0 / 64, p.nqb - 1)];
-    ksh = p.ks + (size_t)bh * p.nkb;
-    vsh = p.vs + (size_t)bh * p.nkb;
+    cq = p.c * ((gfloat*)p.qs)[(size_t)bh * p.nqb + min(cx.qw0 / 64, p.nqb - 1)];
+    ksh = (gfloat*)(p.ks + (size_t)bh * p.nkb);
+    vsh = (gfloat*)(p.vs + (size_t)bh * p.nkb);
     if (nt > 0) read_scales(0);
   }
   // Step j: K_j, V_j in (Kc, Vc); tile j + 1 -> (Kl, Vl).

@@ -37,9 +37,11 @@
 // about 300 VALU cycles per iteration.  It runs with one or two waves per
 // SIMD, with the A operands in registers or read from LDS one 16-byte read
 // per MFMA (the P V operands optionally by two ds_read_b64_tr_b16, as the
-// kernels read V), and optionally with a workgroup barrier per iteration.
-// Matrix-core use = 512 cycles x waves per SIMD over the slowest wave's
-// cycles per iteration.
+// kernels read V), optionally with a workgroup barrier per iteration, with
+// the kernels' full softmax mix (a row max and v_dot2 row sums added), and
+// with the LDS reads as the compiler schedules them or pinned ahead of
+// their use.  Matrix-core use = 512 cycles x waves per SIMD over the
+// slowest wave's cycles per iteration.
 //
 // A third table gives the CU's LDS read rate: every wave issues `n` reads
 // (ds_read_b128 or ds_read_b64_tr_b16, conflict-free addresses), waits for
@@ -165,8 +167,12 @@ __global__ void __launch_bounds__(512) ceiling_kernel(float* sink, long long* cy
 }
 
 // One attention-like step per iteration (see the header).  MODE bits:
-// 1 = barrier per iteration, 2 = A operands from LDS, 4 = P V operands by
-// transpose reads (with 2).
+// 1 = barrier per iteration, 2 = A operands from LDS (a per-lane base plus
+// immediate offsets, two ring stages, as the kernels address K and V),
+// 4 = P V operands by transpose reads (with 2), 8 = the kernels' full
+// softmax mix (a row max by v_max3 and v_dot2 row sums as well), 16 = the
+// LDS reads pinned by sched_group_barrier: two score reads ahead of their
+// MFMAs and the first two P V reads issued before the softmax (with 2).
 template <int MODE>
 __global__ void __launch_bounds__(512) step_kernel(const f16x8* ain, float* sink, long long* cycles, int iters,
                                                    float c, float m) {
@@ -175,9 +181,11 @@ __global__ void __launch_bounds__(512) step_kernel(const f16x8* ain, float* sink
   typedef short i16x4 __attribute__((ext_vector_type(4)));
   typedef _Float16 lds_f16x8 __attribute__((ext_vector_type(8), address_space(3)));
   typedef short lds_i16x4 __attribute__((ext_vector_type(4), address_space(3)));
-  __shared__ __attribute__((aligned(1024))) _Float16 lds[8192];  // 16 KB: 1024 16-byte operands
+  constexpr bool kLds = MODE & 2, kTr = (MODE & 6) == 6, kMix = MODE & 8, kPin = (MODE & 18) == 18;
+  // 32 KB: two stages of 16 operands of 1 KB (64 lanes x 16 bytes)
+  __shared__ __attribute__((aligned(1024))) _Float16 lds[16384];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int i = threadIdx.x; i < 8192; i += blockDim.x) lds[i] = (_Float16)(0.001f * ((i * 37) % 97));
+  for (int i = threadIdx.x; i < 16384; i += blockDim.x) lds[i] = (_Float16)(0.001f * ((i * 37) % 97));
   __syncthreads();
   f16x8 a[8], pf[2];
   for (int k = 0; k < 8; ++k) a[k] = ain[lane + 64 * k];
@@ -186,16 +194,35 @@ __global__ void __launch_bounds__(512) step_kernel(const f16x8* ain, float* sink
     pf[1][i] = (_Float16)0.25f;
   }
   f32x16 o[4] = {};
-  const lds_f16x8* L = (const lds_f16x8*)lds;
-  const long long t0 = __builtin_readcyclecounter();
-#pragma nounroll
-  for (int it = 0; it < iters; ++it) {
+  float mx = 0.f, l = 0.f;
+  const lds_f16x8* L = (const lds_f16x8*)lds + lane;
+  auto operand = [&](const lds_f16x8* S, int k) -> f16x8 {
+    if constexpr (kTr) {
+      const __attribute__((address_space(3))) char* base = (const __attribute__((address_space(3))) char*)(S + 64 * k);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)base);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8));
+      return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return S[64 * k];
+    }
+  };
+  auto step = [&](const lds_f16x8* S) {
+    // Without a barrier the operands would be loop-invariant loads that the
+    // compiler could hoist out of the loop; the empty asm's memory clobber
+    // makes every step read them again.
     if constexpr (MODE & 1) __syncthreads();
+    else asm volatile("" ::: "memory");
     f32x16 s = {};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const f16x8 av = (MODE & 2) ? L[(lane + 64 * k + 7 * it) & 1023] : a[k];
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pf[k & 1], s, 0, 0, 0);
+    for (int k = 0; k < 8; ++k) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kLds ? S[64 * k] : a[k], pf[k & 1], s, 0, 0, 0);
+    if constexpr (kMix) {
+      float ma = s[0], mb = s[1];
+#pragma unroll
+      for (int r = 2; r < 16; r += 2) {
+        ma = fmaxf(fmaxf(ma, s[r]), s[r]);
+        mb = fmaxf(fmaxf(mb, s[r + 1]), s[r + 1]);
+      }
+      mx = fmaxf(mx, fmaxf(ma, mb));
     }
     float pr[16];
 #pragma unroll
@@ -207,24 +234,38 @@ __global__ void __launch_bounds__(512) step_kernel(const f16x8* ain, float* sink
         const f16x2 t = __builtin_convertvector((f32x2){pr[8 * h + 2 * e], pr[8 * h + 2 * e + 1]}, f16x2);
         pf[h][2 * e] = t[0];
         pf[h][2 * e + 1] = t[1];
+        if constexpr (kMix) l = __builtin_amdgcn_fdot2(t, (f16x2){(_Float16)1.0f, (_Float16)1.0f}, l, false);
       }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      f16x8 av;
-      const int idx = (lane + 64 * (k + 8) + 5 * it) & 1023;
-      if constexpr ((MODE & 6) == 6) {
-        const __attribute__((address_space(3))) char* base = (const __attribute__((address_space(3))) char*)lds;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * idx));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + ((16 * idx) ^ 8)));
-        av = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      } else {
-        av = (MODE & 2) ? L[idx] : a[k];
+    for (int k = 0; k < 8; ++k)
+      o[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kLds ? operand(S, 8 + k) : a[k], pf[k & 1], o[k & 3], 0, 0, 0);
+    if constexpr (kPin) {
+      // two score reads, then (MFMA, read) x 6, two MFMAs; two P V reads;
+      // the softmax; then each P V MFMA with the next read
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      o[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pf[k & 1], o[k & 3], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kTr ? 4 : 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 1000, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, kTr ? 2 : 1, 0);
+      }
     }
+  };
+  const long long t0 = __builtin_readcyclecounter();
+#pragma nounroll
+  for (int it = 0; it < iters; it += 2) {
+    step(L);
+    step(L + 1024);
   }
   const long long t1 = __builtin_readcyclecounter();
-  float acc = 0.f;
+  float acc = mx + l;
   for (int j = 0; j < 4; ++j)
     for (int i = 0; i < 16; ++i) acc += o[j][i];
   sink[blockIdx.x * 512 + threadIdx.x] = acc;
@@ -466,6 +507,9 @@ int main(int argc, char** argv) {
   step_row<3>("operands from LDS, barrier per iteration", 8, ain, sink, cyc, seconds);
   step_row<7>("operands from LDS, P V operands by transpose reads, barrier per iteration", 8, ain, sink, cyc,
               seconds);
+  step_row<9>("full softmax mix, operands in registers, barrier", 8, ain, sink, cyc, seconds);
+  step_row<15>("full softmax mix, operands from LDS (transpose reads for P V), barrier", 8, ain, sink, cyc, seconds);
+  step_row<31>("the same with the LDS reads pinned ahead", 8, ain, sink, cyc, seconds);
   std::printf("\n| LDS read | waves per CU | reads in flight per wave | bytes per clock per CU |\n|---|---|---|---|\n");
   lds_row<false, 2>(8, sink, cyc, seconds);
   lds_row<false, 4>(8, sink, cyc, seconds);

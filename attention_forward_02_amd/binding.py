@@ -98,9 +98,9 @@ def load_library(path=LIB_PATH):
     lib.attn_fwd_fp8_blockscaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
     lib.attn_fwd_fp8_blockscaled.restype = ci
     ull = ctypes.c_ulonglong
-    lib.attn_fwd_splitkv_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci, ci]
+    lib.attn_fwd_splitkv_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
     lib.attn_fwd_splitkv_workspace_bytes.restype = ull
-    lib.attn_fwd_splitkv_num_splits.argtypes = [ci, ci, ci, ci, ci, ci, ci]
+    lib.attn_fwd_splitkv_num_splits.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
     lib.attn_fwd_splitkv_num_splits.restype = ci
     lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, cf, cf, cf, ci, vp, ull, vp]
     lib.attn_fwd_splitkv.restype = ci
@@ -175,16 +175,16 @@ def attn_fwd_fp8_blockscaled(q, k, v, q_descales, k_descales, v_descales, o, lse
                                         int(d), int(bool(causal)), float(scale), _stream(stream))
 
 
-def attn_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, num_splits=0):
+def attn_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, causal, dtype, num_splits=0):
     """The C ``attn_fwd_splitkv_workspace_bytes`` (0 for an unsupported d or dtype)."""
-    return int(load_library().attn_fwd_splitkv_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(d), int(dtype),
-                                                               int(num_splits)))
+    return int(load_library().attn_fwd_splitkv_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(d),
+                                                               int(bool(causal)), int(dtype), int(num_splits)))
 
 
-def attn_fwd_splitkv_num_splits(B, H, Nq, Nk, d, dtype, num_splits=0):
+def attn_fwd_splitkv_num_splits(B, H, Nq, Nk, d, causal, dtype, num_splits=0):
     """The C ``attn_fwd_splitkv_num_splits``."""
-    return int(load_library().attn_fwd_splitkv_num_splits(int(B), int(H), int(Nq), int(Nk), int(d), int(dtype),
-                                                          int(num_splits)))
+    return int(load_library().attn_fwd_splitkv_num_splits(int(B), int(H), int(Nq), int(Nk), int(d),
+                                                          int(bool(causal)), int(dtype), int(num_splits)))
 
 
 def attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, q_descale, k_descale, v_descale,
@@ -299,15 +299,16 @@ def attention(q, k, v, causal=False, scale=None, descale=None, stream=None, vari
     return o, lse
 
 
-def splitkv_workspace(q, k, num_splits=0):
+def splitkv_workspace(q, k, num_splits=0, causal=False):
     """A device workspace (uint8 tensor, possibly empty) for
-    ``attention_splitkv`` on inputs shaped like q and k, reusable by later
-    calls on the same stream."""
+    ``attention_splitkv`` on inputs shaped like q and k with the same
+    num_splits and causal flag, reusable by later calls on the same
+    stream."""
     import torch
     B, H, Nq, d = q.shape
-    if attn_fwd_splitkv_num_splits(B, H, Nq, k.shape[2], d, _dtype_code(q), num_splits) == 0:
+    if attn_fwd_splitkv_num_splits(B, H, Nq, k.shape[2], d, causal, _dtype_code(q), num_splits) == 0:
         raise ValueError("unsupported head dim or dtype")
-    n = attn_fwd_splitkv_workspace_bytes(B, H, Nq, k.shape[2], d, _dtype_code(q), num_splits)
+    n = attn_fwd_splitkv_workspace_bytes(B, H, Nq, k.shape[2], d, causal, _dtype_code(q), num_splits)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
 
 
@@ -324,7 +325,7 @@ def attention_splitkv(q, k, v, causal=False, scale=None, descale=None, num_split
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        workspace = splitkv_workspace(q, k, num_splits)
+        workspace = splitkv_workspace(q, k, num_splits, causal)
     elif not getattr(workspace, "is_cuda", False) or workspace.device != q.device:
         raise ValueError("workspace must be a tensor on q's device")
     out_dtype = torch.bfloat16 if code == ATTN_BF16 else torch.float16

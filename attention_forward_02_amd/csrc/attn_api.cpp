@@ -133,7 +133,7 @@ int run_splitkv(const void* q, const void* k, const void* v, void* o, float* lse
   st = check_scales(scale, q_ds, k_ds, v_ds);
   if (st != ATTN_OK) return st;
   if (num_splits < 0) return ATTN_ERR_SHAPE;
-  const size_t need = attn::splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, num_splits);
+  const size_t need = attn::splitkv_workspace_bytes(B, H, Nq, Nk, d, causal, dtype, num_splits);
   if (need > 0) {
     if (!ws || !aligned(ws, 256) || ws_bytes < need) return ATTN_ERR_WORKSPACE;
     const size_t in_elt = dtype == ATTN_FP8_E4M3 ? 1 : 2;
@@ -243,15 +243,15 @@ int attn_fwd_fp8_blockscaled(const void* q, const void* k, const void* v, const 
   return attn::launch_forward(p, (hipStream_t)stream);
 }
 
-unsigned long long attn_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype,
+unsigned long long attn_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int causal, int dtype,
                                                     int num_splits) {
   if (!splitkv_args_ok(B, H, Nq, Nk, d, dtype, num_splits)) return 0;
-  return attn::splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, num_splits);
+  return attn::splitkv_workspace_bytes(B, H, Nq, Nk, d, causal, dtype, num_splits);
 }
 
-int attn_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits) {
+int attn_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int d, int causal, int dtype, int num_splits) {
   if (!splitkv_args_ok(B, H, Nq, Nk, d, dtype, num_splits)) return 0;
-  return attn::splitkv_splits(B, H, Nq, Nk, d, dtype, num_splits);
+  return attn::splitkv_splits(B, H, Nq, Nk, d, causal, dtype, num_splits);
 }
 
 int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
@@ -267,7 +267,7 @@ int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* 
   int st = validate(q, k, v, o, lse, B, H, Nq, Nk, d, dtype);
   if (st != ATTN_OK) return st;
   if (num_splits < 0) return ATTN_ERR_SHAPE;
-  const size_t need = attn::splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, num_splits);
+  const size_t need = attn::splitkv_workspace_bytes(B, H, Nq, Nk, d, causal, dtype, num_splits);
   if (need > (size_t)ATTN_SPLITKV_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
   void* ws = nullptr;
   if (need > 0) {

@@ -47,6 +47,7 @@ struct SplitSlotsPerCU {
 
 constexpr int kSplitMaxSplits = 32;
 constexpr int kSplitMinTiles = 2;  // key tiles per split at least (auto choice)
+constexpr int kSplitTwoMinKeys = 2048;  // keys a two-way split needs (auto choice)
 constexpr int kCUs = 256;
 
 // How a shape is split.  items = B * H * query tiles; nsplit = splits per
@@ -60,7 +61,7 @@ struct SplitPlan {
 __host__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 template <int D, int DT>
-__host__ inline SplitPlan split_plan(int B, int H, int Nq, int Nk, int num_splits) {
+__host__ inline SplitPlan split_plan(int B, int H, int Nq, int Nk, bool causal, int num_splits) {
   constexpr int kRows = Waves<D, DT>::value * kRowsPerWave;
   constexpr int BN = TileKeys<D, DT>::value;
   SplitPlan sp;
@@ -68,16 +69,26 @@ __host__ inline SplitPlan split_plan(int B, int H, int Nq, int Nk, int num_split
   const int nt_max = (Nk + BN - 1) / BN;
   int s = num_splits;
   if (s <= 0) {
-    // auto: split only grids of fewer query tiles than CUs, into enough
-    // workgroups to fill every CU's slots, with at least kSplitMinTiles key
-    // tiles per split.  (A grid with a tile per CU is not helped: at
-    // B=4 H=8 N=1024 d=64 causal, four splits measured 17.8 us in the split
-    // kernel alone against 17.5 us unsplit -- the per-split Q and K/V loads
-    // and partial writes cost what the shorter key loops save.)
+    // auto: split only grids of fewer query tiles than CUs.  Without causal
+    // masking, into as many workgroups as fit every CU's slots in one round
+    // (more would run a second round of equal-length loops: two splits of
+    // 192 tiles measured up to 1.5x slower); with it, into enough to fill
+    // them (the diagonal tiles' long loops dominate: three splits of 96
+    // causal tiles measured 13-29% faster than two).  At least
+    // kSplitMinTiles key tiles per split.  (A grid with a tile per CU is not
+    // helped: at B=4 H=8 N=1024 d=64 causal, four splits measured 17.8 us
+    // in the split kernel alone against 17.5 us unsplit -- the per-split Q
+    // and K/V loads and partial writes cost what the shorter key loops
+    // save.)
     const long long slots = (long long)kCUs * SplitSlotsPerCU<D, DT>::value;
-    s = sp.items >= kCUs ? 1 : (int)((slots + sp.items - 1) / sp.items);
+    if (sp.items >= kCUs) s = 1;
+    else if (causal) s = (int)((slots + sp.items - 1) / sp.items);
+    else s = (int)(slots / sp.items);
     const int most = nt_max / kSplitMinTiles > 1 ? nt_max / kSplitMinTiles : 1;
     if (s > most) s = most;
+    // A two-way split of equal-length key loops pays for its merge only on
+    // long key ranges.
+    if (!causal && s == 2 && Nk < kSplitTwoMinKeys) s = 1;
   }
   if (s > kSplitMaxSplits) s = kSplitMaxSplits;
   if (s > nt_max) s = nt_max;
@@ -266,7 +277,7 @@ template <int D, int DT, bool CAUSAL>
 int launch_splitkv_one(const Problem& pr, hipStream_t stream) {
   constexpr int kWaves = Waves<D, DT>::value;
   constexpr int kBlockM = kWaves * kRowsPerWave;
-  const SplitPlan sp = split_plan<D, DT>(pr.B, pr.H, pr.Nq, pr.Nk, pr.num_splits);
+  const SplitPlan sp = split_plan<D, DT>(pr.B, pr.H, pr.Nq, pr.Nk, pr.causal != 0, pr.num_splits);
   if (sp.bytes > pr.workspace_bytes || (sp.bytes > 0 && !pr.workspace)) return ATTN_ERR_WORKSPACE;
   const long long grid = 8LL * ((sp.items + 7) / 8) * sp.nsplit;
   if (sp.items > 0x7fffffffLL || grid > 0x7fffffffLL) return ATTN_ERR_SHAPE;

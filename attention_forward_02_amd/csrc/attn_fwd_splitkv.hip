@@ -33,16 +33,16 @@ ATTN_SPLITKV_INSTANCES(256)
 #undef ATTN_SPLITKV_INSTANCES
 
 template <int D>
-SplitPlan plan_d(int B, int H, int Nq, int Nk, int dtype, int num_splits) {
-  if (dtype == ATTN_FP8_E4M3) return split_plan<D, ATTN_FP8_E4M3>(B, H, Nq, Nk, num_splits);
-  return split_plan<D, ATTN_F16>(B, H, Nq, Nk, num_splits);  // bf16 tiles are the same
+SplitPlan plan_d(int B, int H, int Nq, int Nk, bool causal, int dtype, int num_splits) {
+  if (dtype == ATTN_FP8_E4M3) return split_plan<D, ATTN_FP8_E4M3>(B, H, Nq, Nk, causal, num_splits);
+  return split_plan<D, ATTN_F16>(B, H, Nq, Nk, causal, num_splits);  // bf16 tiles are the same
 }
 
-SplitPlan plan(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits) {
+SplitPlan plan(int B, int H, int Nq, int Nk, int d, bool causal, int dtype, int num_splits) {
   switch (d) {
-    case 64: return plan_d<64>(B, H, Nq, Nk, dtype, num_splits);
-    case 128: return plan_d<128>(B, H, Nq, Nk, dtype, num_splits);
-    default: return plan_d<256>(B, H, Nq, Nk, dtype, num_splits);
+    case 64: return plan_d<64>(B, H, Nq, Nk, causal, dtype, num_splits);
+    case 128: return plan_d<128>(B, H, Nq, Nk, causal, dtype, num_splits);
+    default: return plan_d<256>(B, H, Nq, Nk, causal, dtype, num_splits);
   }
 }
 
@@ -63,12 +63,12 @@ int launch_d(const Problem& p, hipStream_t s) {
 
 }  // namespace kernels
 
-size_t splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits) {
-  return kernels::plan(B, H, Nq, Nk, d, dtype, num_splits).bytes;
+size_t splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int causal, int dtype, int num_splits) {
+  return kernels::plan(B, H, Nq, Nk, d, causal != 0, dtype, num_splits).bytes;
 }
 
-int splitkv_splits(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits) {
-  return kernels::plan(B, H, Nq, Nk, d, dtype, num_splits).nsplit;
+int splitkv_splits(int B, int H, int Nq, int Nk, int d, int causal, int dtype, int num_splits) {
+  return kernels::plan(B, H, Nq, Nk, d, causal != 0, dtype, num_splits).nsplit;
 }
 
 namespace {

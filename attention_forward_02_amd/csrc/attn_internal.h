@@ -37,8 +37,8 @@ int launch_forward(const Problem& p, hipStream_t stream);
 
 // Split-key forward: workspace bytes a shape needs (0 for an unsupported
 // head dim or dtype), and the launch.
-size_t splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits);
-int splitkv_splits(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits);
+size_t splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int causal, int dtype, int num_splits);
+int splitkv_splits(int B, int H, int Nq, int Nk, int d, int causal, int dtype, int num_splits);
 int launch_splitkv(const Problem& p, hipStream_t stream);
 // Device address of the current device's static split-key scratch
 // (ATTN_SPLITKV_SCRATCH_BYTES), looked up on the first call per device.

@@ -245,19 +245,22 @@ int attn_fwd_fp8_blockscaled(const void* q, const void* k, const void* v,
 
 /*
  * attn_fwd_splitkv_workspace_bytes: device workspace, in bytes, that
- * attn_fwd_splitkv needs for this shape and num_splits (0 = the library's
- * choice): 0 when the shape is not split, and 0 for invalid arguments (use
- * attn_fwd_splitkv_num_splits to tell them apart).  Host-only.
+ * attn_fwd_splitkv needs for this shape, causal flag and num_splits (0 =
+ * the library's choice, which depends on causal): 0 when the shape is not
+ * split, and 0 for invalid arguments (use attn_fwd_splitkv_num_splits to
+ * tell them apart).  Host-only.
  */
-unsigned long long attn_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int dtype,
-                                                    int num_splits);
+unsigned long long attn_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int causal,
+                                                    int dtype, int num_splits);
 
 /*
  * attn_fwd_splitkv_num_splits: the number of key splits per query tile at
- * most that attn_fwd_splitkv uses for this shape and num_splits request
- * (1 = no split), or 0 if d or dtype is not supported.  Host-only.
+ * most that attn_fwd_splitkv uses for this shape, causal flag and
+ * num_splits request (1 = no split), or 0 if d or dtype is not supported.
+ * Host-only.
  */
-int attn_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int d, int dtype, int num_splits);
+int attn_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int d, int causal, int dtype,
+                                int num_splits);
 
 /*
  * attn_fwd_splitkv: the same forward with the key range of each query tile
@@ -273,8 +276,10 @@ int attn_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int d, int dtype, 
  *
  * Arguments as attn_fwd_variant without `variant`, plus:
  * num_splits       key splits per query tile at most; 0 = the library's
- *                  choice (enough workgroups to fill the CUs, at least two
- *                  key tiles per split); 1 = no split (one launch)
+ *                  choice (grids of fewer query tiles than CUs only; as
+ *                  many workgroups as fit the CUs in one round, or, with
+ *                  causal masking, enough to fill them; at least two key
+ *                  tiles per split); 1 = no split (one launch)
  * workspace        device memory of at least
  *                  attn_fwd_splitkv_workspace_bytes(...) bytes (0 when the
  *                  shape is not split; then it may be NULL), 256-byte

@@ -217,12 +217,12 @@ def test_binding_raises_without_library(tmp_path):
 # Split-key forward: workspace sizing and validation (host only)
 # ---------------------------------------------------------------------------
 
-def _ws(B, H, Nq, Nk, d, dtype=0, ns=0):
-    return _lib().attn_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, dtype, ns)
+def _ws(B, H, Nq, Nk, d, dtype=0, ns=0, causal=0):
+    return _lib().attn_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, causal, dtype, ns)
 
 
-def _nsplit(B, H, Nq, Nk, d, dtype=0, ns=0):
-    return _lib().attn_fwd_splitkv_num_splits(B, H, Nq, Nk, d, dtype, ns)
+def _nsplit(B, H, Nq, Nk, d, dtype=0, ns=0, causal=0):
+    return _lib().attn_fwd_splitkv_num_splits(B, H, Nq, Nk, d, causal, dtype, ns)
 
 
 def test_splitkv_plan():
@@ -240,7 +240,18 @@ def test_splitkv_plan():
     # a single query tile over a long key range splits up to 32 ways, at
     # least two key tiles each
     assert _nsplit(1, 1, 100, 1 << 16, 128) == 32
-    assert _nsplit(1, 1, 100, 256, 128) == 2
+    assert _nsplit(1, 1, 100, 512, 128) == 4
+    # without masking, splits fill the CUs in one round, never two: 128
+    # query tiles of 256 rows split two ways, 192 not at all ...
+    assert _nsplit(1, 16, 2048, 2048, 128) == 2 and _nsplit(1, 24, 2048, 2048, 128) == 1
+    # ... and a two-way split needs at least 2,048 keys to pay for its merge
+    assert _nsplit(1, 16, 2048, 1024, 128) == 1 and _nsplit(1, 1, 100, 256, 128) == 1
+    # with causal masking the splits fill the slots, rounding up: 96 query
+    # tiles of 256 rows split three ways, 192 two ways, even on short ranges
+    assert _nsplit(1, 24, 1024, 1024, 128, causal=1) == 3
+    assert _nsplit(1, 24, 2048, 2048, 128, causal=1) == 2
+    assert _nsplit(1, 1, 100, 256, 128, causal=1) == 2
+    assert _ws(1, 24, 2048, 2048, 128, causal=1) > 0 == _ws(1, 24, 2048, 2048, 128)
     # explicit requests: clamped to the key tiles, rounded to equal tile counts
     assert _nsplit(1, 1, 64, 640, 64, ns=3) == 3      # 10 tiles -> 4 + 4 + 2
     assert _nsplit(1, 1, 64, 640, 64, ns=100) == 10
@@ -260,7 +271,7 @@ def _splitkv(ws=WS, ws_bytes=None, ns=0, **kw):
     a = dict(GOOD)
     a.update(kw)
     if ws_bytes is None:
-        ws_bytes = _ws(a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["dtype"], max(ns, 0))
+        ws_bytes = _ws(a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["dtype"], max(ns, 0), a["causal"])
     return _lib().attn_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
                                    a["causal"], a["scale"], a["dtype"], 1.0, 1.0, 1.0, ns, ws, ws_bytes, None)
 
@@ -277,7 +288,7 @@ def _splitkv(ws=WS, ws_bytes=None, ns=0, **kw):
 def test_splitkv_validation_rejects_before_launch(kw, code):
     a = dict(GOOD)
     a.update({k: v for k, v in kw.items() if k in a})
-    assert _ws(a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["dtype"], max(kw.get("ns", 0), 0)) > 0 or code not in (
+    assert _ws(a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["dtype"], max(kw.get("ns", 0), 0), a["causal"]) > 0 or code not in (
         b.ATTN_ERR_WORKSPACE,)
     assert _splitkv(**kw) == code
 

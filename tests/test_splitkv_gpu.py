@@ -32,7 +32,7 @@ CODES = {"f16": ATTN_F16, "bf16": ATTN_BF16, "e4m3": ATTN_FP8_E4M3}
 def _run(inp, num_splits=0, workspace=None):
     q, k, v = (upload(t, inp.dtype) for t in (inp.q, inp.k, inp.v))
     desc = tuple(float(x) for x in inp.descale) if inp.dtype == "e4m3" else None
-    ws = workspace if workspace is not None else splitkv_workspace(q, k, num_splits)
+    ws = workspace if workspace is not None else splitkv_workspace(q, k, num_splits, inp.causal)
     o, lse = attention_splitkv(q, k, v, causal=inp.causal, scale=float(inp.scale), descale=desc,
                                num_splits=num_splits, workspace=ws)
     torch.cuda.synchronize()
@@ -40,7 +40,7 @@ def _run(inp, num_splits=0, workspace=None):
 
 
 def _check(inp, label, num_splits=0, lse_gate=True, p_abs_v=False):
-    ns = attn_fwd_splitkv_num_splits(inp.B, inp.H, inp.Nq, inp.Nk, inp.d, CODES[inp.dtype], num_splits)
+    ns = attn_fwd_splitkv_num_splits(inp.B, inp.H, inp.Nq, inp.Nk, inp.d, inp.causal, CODES[inp.dtype], num_splits)
     say(f"[gpu] {label}: B={inp.B} H={inp.H} Nq={inp.Nq} Nk={inp.Nk} d={inp.d} causal={inp.causal} "
         f"{inp.dtype} requested splits {num_splits} -> {ns}")
     o, lse, ws = _run(inp, num_splits)

@@ -30,8 +30,8 @@ def _outputs(inp):
 def _both(inp):
     q, k, v = (upload(t, inp.dtype) for t in (inp.q, inp.k, inp.v))
     args = (inp.B, inp.H, inp.Nq, inp.Nk, inp.d, inp.causal, float(inp.scale), CODES[inp.dtype], 1.0, 1.0, 1.0, 0)
-    ns = attn_fwd_splitkv_num_splits(inp.B, inp.H, inp.Nq, inp.Nk, inp.d, CODES[inp.dtype], 0)
-    need = attn_fwd_splitkv_workspace_bytes(inp.B, inp.H, inp.Nq, inp.Nk, inp.d, CODES[inp.dtype], 0)
+    ns = attn_fwd_splitkv_num_splits(inp.B, inp.H, inp.Nq, inp.Nk, inp.d, inp.causal, CODES[inp.dtype], 0)
+    need = attn_fwd_splitkv_workspace_bytes(inp.B, inp.H, inp.Nq, inp.Nk, inp.d, inp.causal, CODES[inp.dtype], 0)
     say(f"[gpu] noalloc vs workspace: B={inp.B} H={inp.H} Nq={inp.Nq} Nk={inp.Nk} d={inp.d} {inp.dtype} "
         f"causal={inp.causal}: {ns} splits, {need} bytes of partials")
     assert ns > 1 and 0 < need

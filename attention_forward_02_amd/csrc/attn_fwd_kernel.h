@@ -1589,10 +1589,12 @@ __device__ __forceinline__ void seq_step128(WaveState<D, DT>& st, const LoopCtxT
   const float c0 = BS ? ts[0].c : cx.c, c1 = BS ? ts[1].c : cx.c;
   constexpr int kRowBytes = D * Fmt<DT>::kBytes;
   constexpr int kHalf = 64 * kRowBytes;
-  // The half-row-sum check of seq_step would keep all eight packed P
-  // fragments live through it: 124-392 bytes of spills at 16-bit d = 128.
-  // So the 128-key step takes the row max first.
-  constexpr bool kSumCheck = false;
+  // The half-row-sum check of seq_step (no row max per tile) at binary16
+  // d = 64 only: 3-4% faster there at B=8 H=8 N=1024 causal and B=2 H=16
+  // N=2048, 1% at B=4 H=8 N=1024 causal; bfloat16 d = 64, which sums the
+  // unrounded p, measured 2-3% slower with it, and at 16-bit d = 128 the
+  // check's live P fragments spill.
+  constexpr bool kSumCheck = D == 64 && DT == ATTN_F16;
   f32x16 s0, s1, s2, s3;
   auto scores = [&]() {
     if constexpr (MASKED) {

@@ -1597,7 +1597,10 @@ __device__ __forceinline__ void seq_step128(WaveState<D, DT>& st, const LoopCtxT
   constexpr bool kSumCheck = D == 64 && DT == ATTN_F16;
   f32x16 s0, s1, s2, s3;
   auto scores = [&]() {
-    if constexpr (MASKED) {
+    // A masked-loop step whose tile needs no bias (the loop starts at an
+    // even tile, so it can take one fully visible tile before the first
+    // that needs one) skips the per-score compare and select.
+    if (MASKED && needs_bias<CAUSAL>(cx, j)) {
       const int rem = cx.visible(j) ? cx.template mask_rem<CAUSAL>(j) : -(1 << 30);
       mask_bias<64>(s0, s1, rem);
       mask_bias<64>(s2, s3, rem - 64);

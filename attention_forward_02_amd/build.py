@@ -21,6 +21,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 # Standalone probe of the chip's MFMA and VALU ceilings (not part of the library).
 CEILING = os.path.join(PKG, "chip_ceiling")
+# Timeline probe: two kernels with their shader-clock trace points, a library
+# of its own (attn_timeline.hip, read by timeline.py).
+TIMELINE_LIB = os.path.join(PKG, "libattn_timeline.so")
 ARCH = "gfx950"
 
 COMMON = [
@@ -60,6 +63,12 @@ SOURCES = [
     ("attn_fwd_splitkv.hip", VGPR_FORM),
     ("attn_quant.hip", []),
 ]
+# The timeline probe's two builds of attn_timeline.hip, each with the options
+# of the library unit that holds its kernel.
+TIMELINE_SOURCES = [
+    ("attn_timeline.hip", VGPR_FORM + ["-DATTN_TIMELINE_KERNEL=0"], "attn_timeline_seq.o"),
+    ("attn_timeline.hip", VGPR_FORM + TRACKERS + ["-DATTN_TIMELINE_KERNEL=1"], "attn_timeline_producer.o"),
+]
 
 
 def hipcc():
@@ -92,12 +101,17 @@ def build(verbose=False):
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
             objs.append(obj)
             cmds.append(compile_command(src, extra, obj))
+        tl_objs = [os.path.join(tmp, name) for _, _, name in TIMELINE_SOURCES]
+        cmds += [compile_command(src, extra, obj) for (src, extra, _), obj in zip(TIMELINE_SOURCES, tl_objs)]
         workers = min(len(cmds), max(1, (os.cpu_count() or 2)))
         with concurrent.futures.ThreadPoolExecutor(workers) as ex:
             list(ex.map(lambda c: _run(c, verbose), cmds))
         out = LIB + ".tmp"
         _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out], verbose)
         os.replace(out, LIB)
+        out = TIMELINE_LIB + ".tmp"
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *tl_objs, "-o", out], verbose)
+        os.replace(out, TIMELINE_LIB)
         exe = os.path.join(tmp, "chip_ceiling")
         _run([hipcc(), *[f for f in COMMON if f != "-fPIC"], os.path.join(CSRC, "chip_ceiling.hip"), "-o", exe], verbose)
         shutil.move(exe, CEILING)

@@ -129,6 +129,57 @@ struct Params {
   // per query tile at most, key tiles per split at most.
   float* part;
   int nsplit, split_tiles;
+#ifdef ATTN_TIMELINE
+  // Timeline probe only (attn_timeline.hip): kTimelineSlots counters per wave.
+  unsigned long long* timeline;
+#endif
+};
+
+// Shader-clock trace points of the timeline probe (attn_timeline.hip, a
+// library of its own).  In the attention library ATTN_TIMELINE is not
+// defined and every member is an empty inline function.  Per wave, lane 0
+// writes: slot 0 the clock at kernel entry, 1 after the Q load and the first
+// tile loads are issued, 2 + j after step j (steps 0 .. kTimelineSteps - 1),
+// and the last four slots the cycles spent waiting at the step barriers, the
+// clock after the output is stored, the step count and the hardware id.
+constexpr int kTimelineSlots = 64;
+constexpr int kTimelineSteps = kTimelineSlots - 6;
+struct Timeline {
+#ifdef ATTN_TIMELINE
+  unsigned long long* slot = nullptr;
+  long long wait = 0, mark0 = 0;
+  bool lane0 = false;
+  __device__ __forceinline__ void init(const Params& p, int waves, int wave) {
+    lane0 = (threadIdx.x & 63) == 0;
+    slot = p.timeline + ((size_t)blockIdx.x * waves + wave) * kTimelineSlots;
+    if (lane0) slot[0] = __builtin_amdgcn_s_memtime();
+  }
+  __device__ __forceinline__ void mark(int i) {
+    if (lane0 && i < kTimelineSlots - 4) slot[i] = __builtin_amdgcn_s_memtime();
+  }
+  __device__ __forceinline__ void step(int j) {
+    if (j < kTimelineSteps) mark(2 + j);
+  }
+  __device__ __forceinline__ void wait_begin() { mark0 = __builtin_amdgcn_s_memtime(); }
+  __device__ __forceinline__ void wait_end() { wait += __builtin_amdgcn_s_memtime() - mark0; }
+  __device__ __forceinline__ void finish(int nt) {
+    unsigned hw;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    if (lane0) {
+      slot[kTimelineSlots - 4] = wait;
+      slot[kTimelineSlots - 3] = __builtin_amdgcn_s_memtime();
+      slot[kTimelineSlots - 2] = nt;
+      slot[kTimelineSlots - 1] = hw;
+    }
+  }
+#else
+  __device__ __forceinline__ void init(const Params&, int, int) {}
+  __device__ __forceinline__ void mark(int) {}
+  __device__ __forceinline__ void step(int) {}
+  __device__ __forceinline__ void wait_begin() {}
+  __device__ __forceinline__ void wait_end() {}
+  __device__ __forceinline__ void finish(int) {}
+#endif
 };
 
 // Input element formats: size and MFMA.
@@ -1733,6 +1784,8 @@ attn_fwd_seq_kernel(Params p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Timeline tl;
+  tl.init(p, kWaves, wave);
   int bh, qt;
   schedule(p, blockIdx.x, CAUSAL, bh, qt);
   const int q0 = qt * kBlockM;
@@ -1794,6 +1847,7 @@ attn_fwd_seq_kernel(Params p) {
     vsh = (gfloat*)(p.vs + (size_t)bh * p.nkb);
     if (nt > 0) read_scales(0);
   }
+  tl.mark(1);
   // Step j: K_j, V_j in (Kc, Vc); tile j + 1 -> (Kl, Vl).
   auto step = [&](int j, const lds_t* Kc, const lds_t* Vc, lds_t* Kl, lds_t* Vl, auto masked) {
     constexpr bool M = decltype(masked)::value;
@@ -1807,7 +1861,9 @@ attn_fwd_seq_kernel(Params p) {
         ts[h].iv = __builtin_amdgcn_rcpf(vd[h]);
       }
     }
+    tl.wait_begin();
     __syncthreads();
+    tl.wait_end();
     if (j + 1 < nt) {
       ld.load(Kl, Kr, (j + 1) * BN);
       ld.load(Vl, Vr, (j + 1) * BN);
@@ -1815,6 +1871,7 @@ attn_fwd_seq_kernel(Params p) {
     }
     if constexpr (BN == 128) seq_step128<D, DT, CAUSAL, M, BS>(st, cx, j, Kc, Vc, ts);
     else seq_step<D, DT, CAUSAL, M, BN, BS>(st, cx, j, Kc, Vc, ts[0]);
+    tl.step(j);
   };
   int j = 0;
   for (; j < jm; j += 2) {
@@ -1827,6 +1884,7 @@ attn_fwd_seq_kernel(Params p) {
     step(j + 1, K1, V1, K0, V0, BoolTag<true>{});
   }
   store_output<D, DT>(p, st, bh, cx.qrow, cx.half);
+  tl.finish(nt);
 }
 
 // ---------------------------------------------------------------------------
@@ -1859,6 +1917,8 @@ __global__ void __launch_bounds__(64 * (8 + NP)) attn_fwd_producer_kernel(Params
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Timeline tl;
+  tl.init(p, kConsumers + NP, wave);
   int bh, qt;
   schedule(p, blockIdx.x, CAUSAL, bh, qt);
   const int q0 = qt * kBlockM;
@@ -1878,13 +1938,17 @@ __global__ void __launch_bounds__(64 * (8 + NP)) attn_fwd_producer_kernel(Params
       ld.load((lds_t*)v_st[s], Vr, t * BN);
     };
     for (int t = 0; t < NS - 1 && t < nt; ++t) issue(t);
+    tl.mark(1);
     for (int j = 0; j < nt; ++j) {
       // Issued so far: tiles 0 .. min(j + NS - 2, nt - 1); tile j must land.
       if (j + NS - 2 < nt) wait_vmcnt<(NS - 2) * kLoads>();
       else wait_vmcnt<0>();
+      tl.wait_begin();
       __syncthreads();
+      tl.wait_end();
       if (j + NS - 1 < nt) issue(j + NS - 1);
     }
+    tl.finish(nt);
     return;  // the consumers' last barrier is the producers' last one
   }
 
@@ -1901,11 +1965,15 @@ __global__ void __launch_bounds__(64 * (8 + NP)) attn_fwd_producer_kernel(Params
   st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane, p.q_and, p.q_xor);
   const int tb = min(first_bias_tile<CAUSAL>(cx), nt);
   const TileScale ts{};
+  tl.mark(1);
   // One barrier per step, nt in all, as on the producer side.
   auto step = [&](int j, int s, auto masked) {
     constexpr bool M = decltype(masked)::value;
+    tl.wait_begin();
     __syncthreads();
+    tl.wait_end();
     seq_step<D, DT, CAUSAL, M, BN, false, false>(st, cx, j, (const lds_t*)k_st[s], (const lds_t*)v_st[s], ts);
+    tl.step(j);
   };
   // Steps run in groups of NS so that each one's stage is a constant.
   const int jm = tb - tb % NS;
@@ -1922,6 +1990,7 @@ __global__ void __launch_bounds__(64 * (8 + NP)) attn_fwd_producer_kernel(Params
     }
   }
   store_output<D, DT>(p, st, bh, cx.qrow, cx.half);
+  tl.finish(nt);
 }
 
 // ---------------------------------------------------------------------------

@@ -315,8 +315,10 @@ def splitkv_workspace(q, k, num_splits=0, causal=False):
 def attention_splitkv(q, k, v, causal=False, scale=None, descale=None, num_splits=0, workspace=None, stream=None):
     """``attention`` through ``attn_fwd_splitkv``: the key range of every
     query tile split over up to ``num_splits`` workgroups (0 = the library's
-    choice) and merged.  ``workspace`` is a device tensor from
-    ``splitkv_workspace`` (allocated here when None)."""
+    choice, which depends on ``causal``) and merged.  ``workspace`` is a
+    device tensor from ``splitkv_workspace`` made with the same num_splits
+    and causal flag (allocated here when None); one too small for the call
+    raises AttnError (ATTN_ERR_WORKSPACE) before anything runs."""
     import torch
     _check_qkv(q, k, v)
     B, H, Nq, d = q.shape

@@ -17,7 +17,10 @@ counts 4*B*H*Nq*Nk*d, halved for causal.
 Prints ONE JSON line: the headline workload's throughput, the MFMA roofline
 of its attention kernel (its own launch time, from HIP events around its
 launches on the stream they run on), every task configuration timed the
-same way in the same process ("configs"), and -- unless --no-cpu -- the CPU
+same way in the same process ("configs"; each also as a captured HIP graph
+of back-to-back steps, replayed: "graph_ms_per_step", the device-side rate
+without the host's launch cost between steps, after three replays matched
+an eager step bit for bit), and -- unless --no-cpu -- the CPU
 leg: the float64 oracle timed on the host's cores on the headline workload
 ("cpu_baseline") and its results compared with this run's GPU outputs of
 every configuration ("parity": max |dO|, elements above 4e-3, max |dLSE|,
@@ -144,7 +147,46 @@ class Case:
         end.record(self.stream)
         torch.cuda.synchronize()
         ms = start.elapsed_time(end) / steps
+        self._last_ms = ms
         return ms, sorted(a.elapsed_time(c) for a, c in marks), burst_ms
+
+    def graph_time(self, budget_ms=20.0, replays=5):
+        """ms per step with as many steps as fit about budget_ms captured in
+        one HIP graph and the graph replayed: the device-side rate without
+        the host's launch cost between steps.  Before timing, three replays
+        (an eager step between each) must give the eager step's outputs bit
+        for bit, else this raises."""
+        torch = self.torch
+        self.step()
+        torch.cuda.synchronize()
+        o_ref, l_ref = self.o.clone(), self.lse.clone()
+        per = max(1, min(100, int(budget_ms / max(self._last_ms, 1e-3))))
+        g = torch.cuda.CUDAGraph()
+        eager_stream = self.stream
+        try:
+            with torch.cuda.graph(g):
+                self.stream = torch.cuda.current_stream()
+                for _ in range(per):
+                    self.step()
+        finally:
+            self.stream = eager_stream
+        for _ in range(3):
+            self.o.zero_()
+            self.lse.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not (torch.equal(self.o.view(torch.int16), o_ref.view(torch.int16)) and torch.equal(self.lse, l_ref)):
+                raise RuntimeError(f"{self.name}: a graph replay differs from the eager step")
+            self.step()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()
+        e0.record(eager_stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(eager_stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (replays * per)
 
     def outputs(self):
         """(O codes as uint16 numpy, LSE float32 numpy) of the last step."""
@@ -394,11 +436,14 @@ def main():
                 c_ms, c_launch, _ = c.time(steps, args.warmup, args.settle)
                 cases[name] = c
             k_ms = sum(c_launch) / len(c_launch)
+            g_ms = c.graph_time()
             pk = PEAK_TFLOPS[c.mma_dtype]
             rows.append({"workload": name, "ms_per_step": round(c_ms, 5), "kernel_ms": round(k_ms, 5),
                          "kernel_ms_median": round(c_launch[len(c_launch) // 2], 5),
+                         "graph_ms_per_step": round(g_ms, 5),
                          "tflops": round(c.flops / (c_ms * 1e-3) / 1e12, 2),
                          "kernel_tflops": round(c.flops / (k_ms * 1e-3) / 1e12, 2),
+                         "graph_tflops": round(c.flops / (g_ms * 1e-3) / 1e12, 2),
                          "peak": pk, "frac": round(c.flops / (k_ms * 1e-3) / 1e12 / pk, 4),
                          "dtype": c.mma_dtype})
         rec["configs"] = rows

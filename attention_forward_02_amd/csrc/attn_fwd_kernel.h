@@ -1805,12 +1805,21 @@ attn_fwd_seq_kernel(Params p) {
   const uint32_t head_bytes = (uint32_t)p.Nk * kRowBytes;
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc(p.k + (size_t)bh * p.Nk * kRowBytes, head_bytes);
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(p.v + (size_t)bh * p.Nk * kRowBytes, head_bytes);
-  TileLoader<D, DT, kWaves, BN> ld;
-  ld.init(wave, lane);
+  // Who issues the K/V tile loads: every wave its share, except at 16-bit
+  // d = 256, where waves 0-3 issue them all.  Wave w shares SIMD w with
+  // wave w + 4 and, being the older one, gets its matrix core first, so
+  // waves 0-3 finish their steps early and wait at the barrier (as the
+  // timeline probe shows for the producer-wave kernel); causal_d256_bf16
+  // measured 1.8% faster with their loads there.  E4M3 d = 128 measured
+  // 1.4% slower (2.5% block-scaled), so it keeps every wave loading.
+  constexpr int kLoadWaves = (D == 256 && DT != ATTN_FP8_E4M3) ? 4 : kWaves;
+  const bool loader = wave < kLoadWaves;
+  TileLoader<D, DT, kLoadWaves, BN> ld;
+  ld.init(loader ? wave : 0, lane);
   WaveState<D, DT> st;
   st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane, p.q_and, p.q_xor);
 
-  if (nt > 0) {
+  if (nt > 0 && loader) {
     ld.load(K0, Kr, 0);
     ld.load(V0, Vr, 0);
   }
@@ -1865,8 +1874,10 @@ attn_fwd_seq_kernel(Params p) {
     __syncthreads();
     tl.wait_end();
     if (j + 1 < nt) {
-      ld.load(Kl, Kr, (j + 1) * BN);
-      ld.load(Vl, Vr, (j + 1) * BN);
+      if (loader) {
+        ld.load(Kl, Kr, (j + 1) * BN);
+        ld.load(Vl, Vr, (j + 1) * BN);
+      }
       if constexpr (BS) read_scales(j + 1);
     }
     if constexpr (BN == 128) seq_step128<D, DT, CAUSAL, M, BS>(st, cx, j, Kc, Vc, ts);

@@ -1805,17 +1805,21 @@ attn_fwd_seq_kernel(Params p) {
   const uint32_t head_bytes = (uint32_t)p.Nk * kRowBytes;
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc(p.k + (size_t)bh * p.Nk * kRowBytes, head_bytes);
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(p.v + (size_t)bh * p.Nk * kRowBytes, head_bytes);
-  // Who issues the K/V tile loads: every wave its share, except at 16-bit
-  // d = 256, where waves 0-3 issue them all.  Wave w shares SIMD w with
-  // wave w + 4 and, being the older one, gets its matrix core first, so
-  // waves 0-3 finish their steps early and wait at the barrier (as the
-  // timeline probe shows for the producer-wave kernel); causal_d256_bf16
-  // measured 1.8% faster with their loads there.  E4M3 d = 128 measured
-  // 1.4% slower (2.5% block-scaled), so it keeps every wave loading.
-  constexpr int kLoadWaves = (D == 256 && DT != ATTN_FP8_E4M3) ? 4 : kWaves;
-  const bool loader = wave < kLoadWaves;
+  // Who issues the K/V tile loads: every wave its share, except in two
+  // 8-wave forms, where four waves issue them all.  Wave w shares SIMD w
+  // with wave w + 4, and one wave of each pair gets the matrix core first
+  // and then waits at the step barrier (the timeline probe shows it for the
+  // producer-wave kernel).  Which four pays was measured: at 16-bit d = 256
+  // waves 0-3 (causal_d256_bf16 1.8% faster; waves 4-7 2% slower), at E4M3
+  // d = 128 waves 4-7 (0.8% faster, block-scaled 1.2%; waves 0-3 1.4% and
+  // 2.5% slower).
+  constexpr bool kE4M3Hi = D == 128 && DT == ATTN_FP8_E4M3;
+  constexpr int kLoadFirst = kE4M3Hi ? 4 : 0;
+  constexpr int kLoadWaves = ((D == 256 && DT != ATTN_FP8_E4M3) || kE4M3Hi) ? 4 : kWaves;
+  const int lw = wave - kLoadFirst;
+  const bool loader = lw >= 0 && lw < kLoadWaves;
   TileLoader<D, DT, kLoadWaves, BN> ld;
-  ld.init(loader ? wave : 0, lane);
+  ld.init(loader ? lw : 0, lane);
   WaveState<D, DT> st;
   st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane, p.q_and, p.q_xor);
 

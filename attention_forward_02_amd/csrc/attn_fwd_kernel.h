@@ -954,8 +954,19 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_kernel(Pa
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc(p.k + (size_t)bh * p.Nk * kRowBytes, head_bytes);
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(p.v + (size_t)bh * p.Nk * kRowBytes, head_bytes);
 
-  TileLoader<D, DT, kWaves> ld;
-  ld.init(wave, lane);
+  // K/V tile loads: in the 8-wave 16-bit form (d = 128) waves 0-3 issue
+  // them all, the four that get their SIMD's matrix core first and then
+  // wait at the step barrier (see the sequential kernel): bfloat16 2.0%
+  // faster (causal 2.2%), binary16 1%, the four-stage ring 3%; waves 4-7
+  // measured no change.  Elsewhere every wave issues its share.
+  constexpr bool kHalfLoad = kWaves == 8 && DT != ATTN_FP8_E4M3;
+  constexpr int kLoadWaves = kHalfLoad ? 4 : kWaves;
+  const bool loader = !kHalfLoad || wave < kLoadWaves;
+  TileLoader<D, DT, kLoadWaves> ldr;
+  ldr.init(loader ? wave : 0, lane);
+  auto load = [&](lds_t* dst, __amdgpu_buffer_rsrc_t src, int key0) {
+    if (loader) ldr.load(dst, src, key0);
+  };
   WaveState<D, DT> st;
   st.init(p.q + (size_t)bh * p.Nq * kRowBytes, cx.qrow, p.Nq, lane, p.q_and, p.q_xor);
 
@@ -973,12 +984,12 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_kernel(Pa
     // the range check; later a stage past the last tile keeps an earlier
     // tile.  Scores of tiles past the end are masked to -inf.
     if (nt > 0) {
-      ld.load(K0, Kr, 0);
-      ld.load(V0, Vr, 0);
-      ld.load(K1, Kr, kBlockN);
-      ld.load(V1, Vr, kBlockN);
-      ld.load(K2, Kr, 2 * kBlockN);
-      if (nt <= 3) ld.load(K3, Kr, 3 * kBlockN);
+      load(K0, Kr, 0);
+      load(V0, Vr, 0);
+      load(K1, Kr, kBlockN);
+      load(V1, Vr, kBlockN);
+      load(K2, Kr, 2 * kBlockN);
+      if (nt <= 3) load(K3, Kr, 3 * kBlockN);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (tb > 0) masked_scores<D, DT, CAUSAL, false>(st, cx, 0, K0, a0, a1);
@@ -991,20 +1002,20 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_kernel(Pa
       constexpr bool M = decltype(masked)::value;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (j + 3 < nt) ld.load(K3, Kr, (j + 3) * kBlockN);
-      if (j + 4 < nt) ld.load(K0, Kr, (j + 4) * kBlockN);
-      if (j + 2 < nt) ld.load(V2, Vr, (j + 2) * kBlockN);
-      if (j + 3 < nt) ld.load(V3, Vr, (j + 3) * kBlockN);
+      if (j + 3 < nt) load(K3, Kr, (j + 3) * kBlockN);
+      if (j + 4 < nt) load(K0, Kr, (j + 4) * kBlockN);
+      if (j + 2 < nt) load(V2, Vr, (j + 2) * kBlockN);
+      if (j + 3 < nt) load(V3, Vr, (j + 3) * kBlockN);
       step<D, DT, CAUSAL, M>(st, cx, j, a0, a1, b0, b1, K1, V0);
       if (j + 1 >= nt) return false;
       step<D, DT, CAUSAL, M>(st, cx, j + 1, b0, b1, a0, a1, K2, V1);
       if (j + 2 >= nt) return false;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (j + 5 < nt) ld.load(K1, Kr, (j + 5) * kBlockN);
-      if (j + 6 < nt) ld.load(K2, Kr, (j + 6) * kBlockN);
-      if (j + 4 < nt) ld.load(V0, Vr, (j + 4) * kBlockN);
-      if (j + 5 < nt) ld.load(V1, Vr, (j + 5) * kBlockN);
+      if (j + 5 < nt) load(K1, Kr, (j + 5) * kBlockN);
+      if (j + 6 < nt) load(K2, Kr, (j + 6) * kBlockN);
+      if (j + 4 < nt) load(V0, Vr, (j + 4) * kBlockN);
+      if (j + 5 < nt) load(V1, Vr, (j + 5) * kBlockN);
       step<D, DT, CAUSAL, M>(st, cx, j + 2, a0, a1, b0, b1, K3, V2);
       if (j + 3 >= nt) return false;
       step<D, DT, CAUSAL, M>(st, cx, j + 3, b0, b1, a0, a1, K0, V3);
@@ -1030,9 +1041,9 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_kernel(Pa
     // K_1 is loaded even when there is no tile 1: its rows then fail the
     // range check and arrive as zeros, so every K stage a step reads holds
     // finite data (scores of tiles past the end are -inf, never NaN).
-    ld.load(K0, Kr, 0);
-    ld.load(V0, Vr, 0);
-    ld.load(K1, Kr, kBlockN);
+    load(K0, Kr, 0);
+    load(V0, Vr, 0);
+    load(K1, Kr, kBlockN);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tb > 0) masked_scores<D, DT, CAUSAL, false>(st, cx, 0, K0, a0, a1);
@@ -1046,15 +1057,15 @@ __global__ void __launch_bounds__(64 * (Waves<D, DT>::value)) attn_fwd_kernel(Pa
     // Even step: (a0, a1) = S_j; K_{j+1} in K1, V_j in V0; K_{j+2} -> K0, V_{j+1} -> V1.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 2 < nt) ld.load(K0, Kr, (j + 2) * kBlockN);
-    if (j + 1 < nt) ld.load(V1, Vr, (j + 1) * kBlockN);
+    if (j + 2 < nt) load(K0, Kr, (j + 2) * kBlockN);
+    if (j + 1 < nt) load(V1, Vr, (j + 1) * kBlockN);
     step<D, DT, CAUSAL, M>(st, cx, j, a0, a1, b0, b1, K1, V0);
     if (j + 1 >= nt) return false;
     // Odd step: (b0, b1) = S_{j+1}; K_{j+2} in K0, V_{j+1} in V1; K_{j+3} -> K1, V_{j+2} -> V0.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 3 < nt) ld.load(K1, Kr, (j + 3) * kBlockN);
-    if (j + 2 < nt) ld.load(V0, Vr, (j + 2) * kBlockN);
+    if (j + 3 < nt) load(K1, Kr, (j + 3) * kBlockN);
+    if (j + 2 < nt) load(V0, Vr, (j + 2) * kBlockN);
     step<D, DT, CAUSAL, M>(st, cx, j + 1, b0, b1, a0, a1, K0, V1);
     return true;
   };

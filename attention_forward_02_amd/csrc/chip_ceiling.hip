@@ -13,6 +13,7 @@
 // over wall time).
 //
 //   mfma f16   every wave: 4 independent v_mfma_f32_32x32x16_f16 chains
+//   mfma bf16  the same with v_mfma_f32_32x32x16_bf16
 //   mfma fp8   every wave: 4 independent v_mfma_f32_32x32x64_f8f6f4 chains
 //              (E4M3 operands)
 //   fma        waves 0-3 only (one wave per SIMD): 16 independent fp32 FMA
@@ -60,7 +61,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 enum { kMfmaF16 = 0, kMfmaFp8 = 1, kFma = 2, kExp = 3, kMfmaFma = 4, kMfmaExp = 5, kLds = 6, kLdsFma = 7, kLdsExp = 8,
-       kExpOnly = 9 };
+       kExpOnly = 9, kMfmaBf16 = 10 };
 constexpr int kCUs = 256;
 constexpr int kWaves = 8;
 
@@ -70,7 +71,7 @@ __global__ void __launch_bounds__(512) ceiling_kernel(float* sink, long long* cy
   constexpr bool kPair = T == kMfmaFma || T == kMfmaExp || T == kLdsFma || T == kLdsExp;
   constexpr bool kUsesLds = T == kLds || T == kLdsFma || T == kLdsExp;
   constexpr bool kExpLoop = T == kExp || T == kMfmaExp || T == kLdsExp;
-  const bool mfma_wave = (T == kMfmaF16 || T == kMfmaFp8 || T == kLds) || (kPair && w < 4);
+  const bool mfma_wave = (T == kMfmaF16 || T == kMfmaFp8 || T == kMfmaBf16 || T == kLds) || (kPair && w < 4);
   const bool valu_wave = ((T == kFma || T == kExp || T == kExpOnly) && w < 4) || (kPair && w >= 4);
   constexpr int kLdsBytes = 16384;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kUsesLds ? kLdsBytes : 16];
@@ -125,6 +126,19 @@ __global__ void __launch_bounds__(512) ceiling_kernel(float* sink, long long* cy
         c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c1, 0, 0, 0, 0, 0, 0);
         c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c2, 0, 0, 0, 0, 0, 0);
         c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c3, 0, 0, 0, 0, 0, 0);
+      }
+    } else if constexpr (T == kMfmaBf16) {
+      typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+      bf16x8 a, b;
+      for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(0.5f + 0.001f * (lane + 7 * i));
+        b[i] = (__bf16)(0.25f - 0.002f * (lane - 3 * i));
+      }
+      for (int it = 0; it < iters; ++it) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
       }
     } else {
       f16x8 a, b;
@@ -475,6 +489,7 @@ int main(int argc, char** argv) {
     std::fflush(stdout);
   };
   row("mfma f16 (4 x 32x32x16 per iteration)", run<kMfmaF16>(iters, seconds, sink, cyc), f16_flop, 2516.6, 8, true);
+  row("mfma bf16 (4 x 32x32x16 per iteration)", run<kMfmaBf16>(iters, seconds, sink, cyc), f16_flop, 2516.6, 8, true);
   row("mfma fp8 (4 x 32x32x64 per iteration)", run<kMfmaFp8>(iters, seconds, sink, cyc), fp8_flop, 5033.2, 8, true);
   row("fma (32 per iteration)", run<kFma>(iters, seconds, sink, cyc), 0, 0, 0, false);
   row("exp (16 exp + 16 mul per iteration)", run<kExp>(iters, seconds, sink, cyc), 0, 0, 0, false);

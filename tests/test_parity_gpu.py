@@ -137,10 +137,21 @@ def test_d64_mid_grid_short_keys(causal, dtype):
 @pytest.mark.parametrize("causal", [False, True])
 def test_d64_large_grid(causal, dtype):
     """d = 64 with more than 512 query tiles of 128 rows: the sequential
-    kernel with 64-key tiles, as for grids of fewer than 64 tiles (the edge
-    shapes)."""
+    kernel with 64-key tiles, as for non-causal grids of fewer than 64
+    tiles with at most 256 keys."""
     inp = inputs.make(2, 17, 2000, 2000, 64, dtype, seed=4242 + int(causal), causal=causal)
     _full_check(inp, f"d64 large grid {'causal' if causal else 'full'} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nk", [200, 700, 2100])
+def test_d64_small_grid(causal, dtype, nk):
+    """d = 64 with fewer than 64 query tiles of 128 rows: the split-key
+    kernel from 2,048 keys, else the 128-key sequential kernel, and the
+    64-key one for a short non-causal key range."""
+    inp = inputs.make(1, 3, 300, nk, 64, dtype, seed=4646 + nk + int(causal), causal=causal)
+    _full_check(inp, f"d64 small grid Nk={nk} {'causal' if causal else 'full'} {dtype}")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])

@@ -1816,15 +1816,16 @@ attn_fwd_seq_kernel(Params p) {
   const uint32_t head_bytes = (uint32_t)p.Nk * kRowBytes;
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc(p.k + (size_t)bh * p.Nk * kRowBytes, head_bytes);
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(p.v + (size_t)bh * p.Nk * kRowBytes, head_bytes);
-  // Who issues the K/V tile loads: every wave its share, except in two
-  // 8-wave forms, where four waves issue them all.  Wave w shares SIMD w
-  // with wave w + 4, and one wave of each pair gets the matrix core first
-  // and then waits at the step barrier (the timeline probe shows it for the
-  // producer-wave kernel).  Which four pays was measured: at 16-bit d = 256
-  // waves 0-3 (causal_d256_bf16 1.8% faster; waves 4-7 2% slower), at E4M3
-  // d = 128 waves 4-7 (0.8% faster, block-scaled 1.2%; waves 0-3 1.4% and
-  // 2.5% slower).
-  constexpr bool kE4M3Hi = D == 128 && DT == ATTN_FP8_E4M3;
+  // Who issues the K/V tile loads: every wave its share, except in the
+  // 8-wave forms at 16-bit d = 256 and at E4M3 (d = 128, 256), where four
+  // waves issue them all.  Wave w shares SIMD w with wave w + 4, and one
+  // wave of each pair gets the matrix core first and then waits at the step
+  // barrier (the timeline probe shows it for the producer-wave kernel).
+  // Which four pays was measured: at 16-bit d = 256 waves 0-3
+  // (causal_d256_bf16 1.8% faster; waves 4-7 2% slower), at E4M3 waves 4-7
+  // (d = 128 0.8% faster, block-scaled 1.2%, d = 256 1.5-1.7%; waves 0-3
+  // 0.7-2.5% slower).
+  constexpr bool kE4M3Hi = DT == ATTN_FP8_E4M3 && kWaves == 8;
   constexpr int kLoadFirst = kE4M3Hi ? 4 : 0;
   constexpr int kLoadWaves = ((D == 256 && DT != ATTN_FP8_E4M3) || kE4M3Hi) ? 4 : kWaves;
   const int lw = wave - kLoadFirst;
